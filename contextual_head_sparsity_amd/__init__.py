@@ -1,0 +1,18 @@
+"""Selective Head Attention (SHA) decode for AMD Instinct MI355X (gfx950).
+
+The compute runs in hand-written HIP kernels behind a C ABI (include/sha.h);
+this package is a thin binding over that library plus the seeded workload
+generator.  The library is loaded on first use and a missing build is an
+error: there is no CPU fallback.
+"""
+from . import workloads
+
+__all__ = ["workloads", "sha_decode", "sha_decode_gqa", "lib"]
+
+
+def __getattr__(name):
+    if name in ("sha_decode", "sha_decode_gqa", "lib", "plan_nsplit", "workspace_bytes",
+                "ShaError"):
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)
