@@ -1,0 +1,153 @@
+"""ctypes binding over libsha.so (include/sha.h): argument marshalling only.
+
+Tensors are PyTorch device tensors (PyTorch supplies device memory and the
+stream); every arithmetic step runs in the library's HIP kernels.  There is
+no fallback: if libsha.so is missing or fails to load, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsha.so")
+
+SHA_F32, SHA_F16, SHA_BF16 = 0, 1, 2
+_DT = {torch.float32: SHA_F32, torch.float16: SHA_F16, torch.bfloat16: SHA_BF16}
+STATUS = {0: "SHA_OK", 1: "SHA_ERR_INVALID_ARG", 2: "SHA_ERR_UNSUPPORTED",
+          3: "SHA_ERR_MISALIGNED", 4: "SHA_ERR_WORKSPACE", 5: "SHA_ERR_HIP"}
+
+# (name, restype, argtypes) for every symbol include/sha.h declares.
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_DECODE_ARGS = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]
+SIGNATURES = {
+    "sha_decode_f32": (_I, _DECODE_ARGS),
+    "sha_decode_f16": (_I, _DECODE_ARGS),
+    "sha_decode_bf16": (_I, _DECODE_ARGS),
+    "sha_decode": (_I, _DECODE_ARGS + [_I]),
+    "sha_decode_gqa_f32": (_I, _DECODE_ARGS),
+    "sha_decode_gqa_f16": (_I, _DECODE_ARGS),
+    "sha_decode_gqa_bf16": (_I, _DECODE_ARGS),
+    "sha_decode_gqa": (_I, _DECODE_ARGS + [_I]),
+    "sha_decode_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
+    "sha_decode_gqa_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
+    "sha_plan_nsplit": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "sha_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "sha_status_string": (ctypes.c_char_p, [_I]),
+    "sha_last_hip_error": (_I, []),
+    "sha_version": (ctypes.c_char_p, []),
+}
+
+
+class ShaError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == 5:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsha.so (built in-tree by contextual_head_sparsity_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m contextual_head_sparsity_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise ShaError(st, where, lib().sha_last_hip_error())
+
+
+def plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa=False, dtype=torch.float16, num_cus=0) -> int:
+    return lib().sha_plan_nsplit(B, H, H_kv, Nkv, d, top_k, int(gqa), _DT[dtype], num_cus)
+
+
+def workspace_bytes(B, H, H_kv, Nkv, d, top_k, gqa=False, dtype=torch.float16, nsplit=0,
+                    num_cus=0) -> int:
+    return lib().sha_workspace_bytes(B, H, H_kv, Nkv, d, top_k, int(gqa), _DT[dtype], nsplit,
+                                     num_cus)
+
+
+def _prepare(q, k, v, index, scale, out, gqa):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one of float32 / float16 / bfloat16")
+    B, H, one, d = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    Bk, H_kv, Nkv, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H_kv, Nkv, d] matching q")
+    if index.dim() != 2 or index.shape[0] != B:
+        raise ValueError("index must be [B, top_k]")
+    if index.device != q.device:
+        raise ValueError("index must be on the same device as q")
+    if index.dtype != torch.int32:
+        index = index.to(torch.int32)
+    index = index.contiguous()
+    top_k = index.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.zeros_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    return B, H, H_kv, Nkv, d, top_k, index, float(scale), out
+
+
+def _call(gqa, q, k, v, index, scale, out, nsplit, workspace, stream):
+    B, H, H_kv, Nkv, d, top_k, index, scale, out = _prepare(q, k, v, index, scale, out, gqa)
+    L = lib()
+    dt = _DT[q.dtype]
+    need = L.sha_workspace_bytes(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = L.sha_decode_gqa_ex if gqa else L.sha_decode_ex
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H, H_kv, Nkv, d,
+                top_k, scale, out.data_ptr(), stream.cuda_stream, dt, nsplit, ws_ptr, need)
+    _check(st, "sha_decode_gqa_ex" if gqa else "sha_decode_ex")
+    return out
+
+
+def sha_decode(q, k, v, batch_head_index, scale=None, out=None, nsplit=0, workspace=None,
+               stream=None):
+    """Head-indexed SHA decode; returns `out` (allocated zeroed when None).
+
+    q [B, H, 1, d], k/v [B, H_kv, Nkv, d], batch_head_index [B, top_k].
+    Slots of `out` not named by the index are left untouched.
+    """
+    return _call(False, q, k, v, batch_head_index, scale, out, nsplit, workspace, stream)
+
+
+def sha_decode_gqa(q, k, v, batch_group_index, scale=None, out=None, nsplit=0, workspace=None,
+                   stream=None):
+    """Group-indexed (GQA group sparsity) SHA decode; see sha_decode."""
+    return _call(True, q, k, v, batch_group_index, scale, out, nsplit, workspace, stream)

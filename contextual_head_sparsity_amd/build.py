@@ -1,0 +1,61 @@
+"""Build the SHA decode library (libsha.so) in-tree for gfx950 with hipcc.
+
+    python -m contextual_head_sparsity_amd.build
+
+Every call compiles from source (no staleness check) and replaces the
+library atomically.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsha.so")
+ARCH = "gfx950"
+
+# Packed-fp32 VALU ops are disabled for all device code; hipcc's host pass
+# warns that it does not know the feature, which is harmless.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
+          "-Wno-unused-command-line-argument"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the SHA library)")
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    hipcc = _hipcc()
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    kern = os.path.join(objdir, "sha_kernels.o")
+    _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
+          os.path.join(CSRC, "sha_kernels.hip"), "-o", kern])
+    objs.append(kern)
+    api = os.path.join(objdir, "sha_api.o")
+    _run([hipcc, "-c", *COMMON, os.path.join(CSRC, "sha_api.cpp"), "-o", api])
+    objs.append(api)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

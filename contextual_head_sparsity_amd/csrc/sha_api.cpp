@@ -1,0 +1,364 @@
+// C ABI of the SHA decode library: host-side validation, split planning,
+// workspace handling and launch.  Declarations and the contract of every
+// entry point are in include/sha.h.
+#include "sha.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "sha_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxGroup = 64;
+
+struct Problem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  void* o;
+  int B, H, H_kv, Nkv, d, top_k;
+  float scale;
+  int dtype;
+  bool gqa;
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Scalar checks, in a fixed order; `empty` is set for B == 0 or top_k == 0.
+sha_status check_scalars(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
+                         bool* empty) {
+  *empty = false;
+  if (B < 0 || top_k < 0 || H < 1 || H_kv < 1 || Nkv < 1 || d < 1) return SHA_ERR_INVALID_ARG;
+  if (H % H_kv != 0) return SHA_ERR_INVALID_ARG;
+  if (dtype != SHA_F32 && dtype != SHA_F16 && dtype != SHA_BF16) return SHA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return SHA_ERR_UNSUPPORTED;
+  if (gqa && H / H_kv > kMaxGroup) return SHA_ERR_UNSUPPORTED;
+  if (top_k > (gqa ? H_kv : H)) return SHA_ERR_INVALID_ARG;
+  if (B == 0 || top_k == 0) *empty = true;
+  return SHA_OK;
+}
+
+int device_cus(int num_cus) {
+  if (num_cus > 0) return num_cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Tuning hooks for sweeps: SHA_MHA_VARIANT / SHA_GQA_VARIANT pick a kernel
+// shape from the table in sha_kernels.hip (0 = default).
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s ? atoi(s) : dflt;
+}
+int mha_variant() {
+  static const int v = env_int("SHA_MHA_VARIANT", 0);
+  return v;
+}
+int gqa_variant() {
+  static const int v = env_int("SHA_GQA_VARIANT", 0);
+  return v;
+}
+
+// Workgroups one split of the whole call launches.
+long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa) {
+  long long per_unit = 1;
+  if (gqa) {
+    const int G = H / H_kv;
+    const int nh = sha::gqa_heads_per_wg(G);
+    per_unit = G == 1 ? 1 : (G + nh - 1) / nh;
+  }
+  return static_cast<long long>(B) * top_k * per_unit;
+}
+
+// Keys one iteration of a workgroup consumes (all lane groups, all unroll
+// steps); splits are sized in whole iterations where possible.
+int rows_per_iter(int d, int dtype, int gqa, int H, int H_kv) {
+  const bool use_gqa = gqa && H / H_kv > 1;
+  const sha::KernelShape s =
+      use_gqa ? sha::gqa_shape(dtype, d, gqa_variant()) : sha::mha_shape(dtype, d, mha_variant());
+  const int vec = dtype == SHA_F32 ? 4 : 8;
+  const int rows_per_wave = 64 / (d / vec);
+  return s.waves * rows_per_wave * s.unroll;
+}
+
+// Split count: enough workgroups to give every CU several (the grid must be
+// much larger than 256 CUs to fill the chip and hide the tail), but no split
+// shorter than two iterations of the split kernel.
+int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
+                int num_cus) {
+  const long long wgs = wgs_per_split(B, H, H_kv, top_k, gqa);
+  if (wgs <= 0) return 1;
+  const long long target = 4LL * device_cus(num_cus);
+  long long ns = (target + wgs - 1) / wgs;
+  const int min_rows = 2 * rows_per_iter(d, dtype, gqa, H, H_kv);
+  const long long max_ns = Nkv / min_rows > 1 ? Nkv / min_rows : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  const int env = env_int("SHA_NSPLIT", 0);
+  if (env > 0) ns = env;
+  return static_cast<int>(ns);
+}
+
+// Effective split geometry: `chunk` keys per split (a multiple of 16 keys
+// when there is more than one split), every split non-empty.
+void split_geometry(int Nkv, int nsplit_req, int* nsplit, int* chunk) {
+  int ns = nsplit_req < 1 ? 1 : (nsplit_req > Nkv ? Nkv : nsplit_req);
+  if (ns == 1) {
+    *nsplit = 1;
+    *chunk = Nkv;
+    return;
+  }
+  int c = (Nkv + ns - 1) / ns;
+  c = (c + 15) / 16 * 16;
+  *chunk = c;
+  *nsplit = (Nkv + c - 1) / c;
+}
+
+size_t partial_bytes(int B, int H, int H_kv, int d, int top_k, int gqa, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t heads = gqa ? static_cast<size_t>(H / H_kv) : 1;
+  const size_t n = static_cast<size_t>(B) * top_k * heads * nsplit;
+  const size_t o_bytes = (n * d * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + n * 2 * sizeof(float);
+}
+
+sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Internal workspace for the calls without an explicit workspace: one
+// grow-only buffer per (device, stream), kept until the process ends.
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+
+sha_status run_auto(const Problem& p, hipStream_t stream) {
+  bool empty = false;
+  sha_status st = check_scalars(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, &empty);
+  if (st != SHA_OK || empty) return st;
+  const int ns_plan = plan_nsplit(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, 0);
+  int ns = 1, chunk = p.Nkv;
+  split_geometry(p.Nkv, ns_plan, &ns, &chunk);
+  const bool gqa_eff = p.gqa && p.H / p.H_kv > 1;
+  const size_t need = partial_bytes(p.B, p.H, p.H_kv, p.d, p.top_k, gqa_eff, ns);
+  if (need == 0) return run(p, ns, nullptr, 0, stream);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return SHA_ERR_HIP;
+  }
+  auto& slot = g_ws[{dev, stream}];
+  if (slot.second < need) {
+    if (slot.first) {
+      // The old buffer may still be read by queued work on this stream.
+      e = hipStreamSynchronize(stream);
+      if (e == hipSuccess) e = hipFree(slot.first);
+      slot = {nullptr, 0};
+      if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return SHA_ERR_HIP;
+      }
+    }
+    void* ptr = nullptr;
+    e = hipMalloc(&ptr, need);
+    if (e != hipSuccess) {
+      g_last_hip_error = e;
+      return SHA_ERR_HIP;
+    }
+    slot = {ptr, need};
+  }
+  return run(p, ns, slot.first, slot.second, stream);
+}
+
+sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipStream_t stream) {
+  bool empty = false;
+  sha_status st = check_scalars(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, &empty);
+  if (st != SHA_OK || empty) return st;
+  if (!p.q || !p.k || !p.v || !p.idx || !p.o) return SHA_ERR_INVALID_ARG;
+  if (!(isfinite(p.scale))) return SHA_ERR_INVALID_ARG;
+  if (!aligned(p.q, 16) || !aligned(p.k, 16) || !aligned(p.v, 16) || !aligned(p.o, 16) ||
+      !aligned(p.idx, 4))
+    return SHA_ERR_MISALIGNED;
+
+  const bool gqa_eff = p.gqa && p.H / p.H_kv > 1;
+  int ns = 1, chunk = p.Nkv;
+  const int req = nsplit_req > 0
+                      ? nsplit_req
+                      : plan_nsplit(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, 0);
+  split_geometry(p.Nkv, req, &ns, &chunk);
+
+  // Grid limit: blocks * threads per block (at most 512) must fit 32 bits.
+  const long long blocks = wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa) * ns;
+  if (blocks > (1LL << 23)) return SHA_ERR_INVALID_ARG;
+
+  sha::Args a{};
+  a.q = p.q;
+  a.k = p.k;
+  a.v = p.v;
+  a.idx = p.idx;
+  a.o = p.o;
+  a.B = p.B;
+  a.H = p.H;
+  a.H_kv = p.H_kv;
+  a.Nkv = p.Nkv;
+  a.top_k = p.top_k;
+  a.G = p.H / p.H_kv;
+  a.nsplit = ns;
+  a.chunk = chunk;
+  a.scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
+
+  const size_t need = partial_bytes(p.B, p.H, p.H_kv, p.d, p.top_k, gqa_eff, ns);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return SHA_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SHA_ERR_MISALIGNED;
+    const size_t heads = gqa_eff ? static_cast<size_t>(a.G) : 1;
+    const size_t n = static_cast<size_t>(p.B) * p.top_k * heads * ns;
+    a.part_o = static_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         (n * p.d * sizeof(float) + 255) / 256 * 256);
+  }
+
+  (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
+  const hipError_t e = gqa_eff ? sha::launch_gqa(a, p.dtype, p.d, gqa_variant(), stream)
+                               : sha::launch_mha(a, p.dtype, p.d, mha_variant(), stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return SHA_ERR_HIP;
+  }
+  return SHA_OK;
+}
+
+Problem make(const void* q, const void* k, const void* v, const int32_t* idx, int B, int H,
+             int H_kv, int Nkv, int d, int top_k, float scale, void* o, int dtype, bool gqa) {
+  return Problem{q, k, v, idx, o, B, H, H_kv, Nkv, d, top_k, scale, dtype, gqa};
+}
+
+}  // namespace
+
+extern "C" {
+
+sha_status sha_decode(const void* q, const void* k, const void* v,
+                      const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv, int d,
+                      int top_k, float scale, void* o, hipStream_t stream, sha_dtype dtype) {
+  return run_auto(make(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype,
+                       false),
+                  stream);
+}
+
+sha_status sha_decode_f32(const void* q, const void* k, const void* v,
+                          const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                          int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                    SHA_F32);
+}
+
+sha_status sha_decode_f16(const void* q, const void* k, const void* v,
+                          const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                          int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                    SHA_F16);
+}
+
+sha_status sha_decode_bf16(const void* q, const void* k, const void* v,
+                           const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                           int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                    SHA_BF16);
+}
+
+sha_status sha_decode_gqa(const void* q, const void* k, const void* v,
+                          const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                          int d, int top_k, float scale, void* o, hipStream_t stream,
+                          sha_dtype dtype) {
+  return run_auto(make(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype,
+                       true),
+                  stream);
+}
+
+sha_status sha_decode_gqa_f32(const void* q, const void* k, const void* v,
+                              const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                              int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode_gqa(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                        SHA_F32);
+}
+
+sha_status sha_decode_gqa_f16(const void* q, const void* k, const void* v,
+                              const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                              int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode_gqa(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                        SHA_F16);
+}
+
+sha_status sha_decode_gqa_bf16(const void* q, const void* k, const void* v,
+                               const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                               int d, int top_k, float scale, void* o, hipStream_t stream) {
+  return sha_decode_gqa(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, stream,
+                        SHA_BF16);
+}
+
+sha_status sha_decode_ex(const void* q, const void* k, const void* v,
+                         const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv, int d,
+                         int top_k, float scale, void* o, hipStream_t stream, sha_dtype dtype,
+                         int nsplit, void* workspace, size_t workspace_bytes) {
+  if (nsplit < 0) return SHA_ERR_INVALID_ARG;
+  return run(make(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype, false),
+             nsplit, workspace, workspace_bytes, stream);
+}
+
+sha_status sha_decode_gqa_ex(const void* q, const void* k, const void* v,
+                             const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                             int d, int top_k, float scale, void* o, hipStream_t stream,
+                             sha_dtype dtype, int nsplit, void* workspace,
+                             size_t workspace_bytes) {
+  if (nsplit < 0) return SHA_ERR_INVALID_ARG;
+  return run(make(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype, true),
+             nsplit, workspace, workspace_bytes, stream);
+}
+
+int sha_plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, sha_dtype dtype,
+                    int num_cus) {
+  bool empty = false;
+  if (check_scalars(B, H, H_kv, Nkv, d, top_k, gqa, dtype, &empty) != SHA_OK) return 0;
+  if (empty) return 1;
+  int ns = 1, chunk = Nkv;
+  split_geometry(Nkv, plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus), &ns, &chunk);
+  return ns;
+}
+
+size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
+                           sha_dtype dtype, int nsplit, int num_cus) {
+  bool empty = false;
+  if (check_scalars(B, H, H_kv, Nkv, d, top_k, gqa, dtype, &empty) != SHA_OK || empty) return 0;
+  const int req = nsplit > 0 ? nsplit : plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus);
+  int ns = 1, chunk = Nkv;
+  split_geometry(Nkv, req, &ns, &chunk);
+  return partial_bytes(B, H, H_kv, d, top_k, gqa && H / H_kv > 1, ns);
+}
+
+const char* sha_status_string(sha_status s) {
+  switch (s) {
+    case SHA_OK: return "SHA_OK";
+    case SHA_ERR_INVALID_ARG: return "SHA_ERR_INVALID_ARG";
+    case SHA_ERR_UNSUPPORTED: return "SHA_ERR_UNSUPPORTED";
+    case SHA_ERR_MISALIGNED: return "SHA_ERR_MISALIGNED";
+    case SHA_ERR_WORKSPACE: return "SHA_ERR_WORKSPACE";
+    case SHA_ERR_HIP: return "SHA_ERR_HIP";
+  }
+  return "SHA_ERR_UNKNOWN";
+}
+
+int sha_last_hip_error(void) { return g_last_hip_error; }
+
+const char* sha_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,492 @@
+// HIP kernels for Selective Head Attention (SHA) decode on gfx950 (CDNA4).
+//
+// The method: Polar Sparsity reproducibility page (ri.k117.org), "Pseudocode",
+// Algorithm 1 "Selective Head Flash Attention (Decode)": each unit (b, k)
+// resolves head_idx = batch_head_index[b, k], streams K/V of that head in
+// tiles while keeping a running max m, running sum l and output accumulator
+// (steps 3-10), then writes O[b, head_idx, 0, :] (step 11).  Only active heads
+// are read and written (Polar Sparsity notes, papernotes.org, "Selective Head
+// Attention (SHA) Kernel").
+//
+// MI355X mapping (our design, not the pages' A100 kernel):
+//   * A workgroup is one (unit, KV split).  Inside it, every aligned group of
+//     LPR = d*elem/16 lanes owns one key row per load: one 128-bit load per
+//     lane per row, so a wave64 reads 64*16 = 1 KiB of contiguous K (or V)
+//     per load instruction.  Each lane group is an independent online-softmax
+//     stream over its rows; streams are merged at the end (shuffles inside a
+//     wave, LDS across waves).  Each K/V byte is consumed by exactly the lane
+//     that loaded it, so K/V go HBM -> VGPR with no LDS round trip.
+//   * q.k partial dot products use v_dot2_f32_{f16,bf16} (exact fp16/bf16
+//     products, fp32 accumulate) and a DPP butterfly inside the lane group.
+//   * Scores carry scale*log2(e), so every exponential is one v_exp_f32 (2^x).
+//   * The running max is only moved when a chunk's max exceeds it by more
+//     than kRescaleSlack (base-2 units): probabilities stay <= 2^8, the final
+//     O = o / l is unchanged, and the per-chunk rescale of o is skipped in the
+//     common case.  This is the same running-max algebra as Algorithm 1
+//     step 8 with a lazier update rule.
+//   * O is accumulated unnormalised and divided by l once at the end (the
+//     value of Algorithm 1 step 9's per-tile normalisation, fewer divides).
+//   * KV split (flash-decoding): a unit's keys are cut into nsplit contiguous
+//     chunks so that small B*top_k still fills 256 CUs; each split writes
+//     fp32 (o, m, l) partials and a second kernel merges them in a fixed
+//     order (the step-8 merge across splits).  The kernel boundary makes the
+//     partials visible across XCDs without atomics.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sha_launch.h"
+
+namespace sha {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+// Lazy-rescale slack in base-2 units: probabilities are bounded by 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of LPR lanes; every lane of the group receives
+// the same total.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "lanes per key row");
+  x += dpp<0xB1>(x);                               // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);                               // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);                              // row_half_mirror (8 lanes)
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);     // row_mirror (16 lanes)
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Element types: 16 bytes per lane per load.
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<kF32> {
+  static constexpr int VEC = 4;
+  __device__ static float dot(uint4 q, uint4 k) {
+    float s = __uint_as_float(q.x) * __uint_as_float(k.x);
+    s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
+    s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
+    return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
+  }
+  __device__ static void widen(uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(void* base, size_t i, float x) { static_cast<float*>(base)[i] = x; }
+};
+
+template <>
+struct Elem<kF16> {
+  static constexpr int VEC = 8;
+  __device__ static float dot(uint4 q, uint4 k) {
+    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.x), __builtin_bit_cast(h2_t, k.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.y), __builtin_bit_cast(h2_t, k.y), s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.z), __builtin_bit_cast(h2_t, k.z), s, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.w), __builtin_bit_cast(h2_t, k.w), s, false);
+  }
+  __device__ static void widen2(uint32_t w, float* f) {
+    const h2_t h = __builtin_bit_cast(h2_t, w);
+    f[0] = static_cast<float>(h.x);
+    f[1] = static_cast<float>(h.y);
+  }
+  __device__ static void widen(uint4 v, float* f) {
+    widen2(v.x, f);
+    widen2(v.y, f + 2);
+    widen2(v.z, f + 4);
+    widen2(v.w, f + 6);
+  }
+  __device__ static void store(void* base, size_t i, float x) {
+    static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
+  }
+};
+
+template <>
+struct Elem<kBF16> {
+  static constexpr int VEC = 8;
+  __device__ static float dot(uint4 q, uint4 k) {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.x), __builtin_bit_cast(b2_t, k.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.y), __builtin_bit_cast(b2_t, k.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.z), __builtin_bit_cast(b2_t, k.z), s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.w), __builtin_bit_cast(b2_t, k.w), s, false);
+  }
+  // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+  __device__ static void widen2(uint32_t w, float* f) {
+    f[0] = __uint_as_float(w << 16);
+    f[1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+  __device__ static void widen(uint4 v, float* f) {
+    widen2(v.x, f);
+    widen2(v.y, f + 2);
+    widen2(v.z, f + 4);
+    widen2(v.w, f + 6);
+  }
+  __device__ static void store(void* base, size_t i, float x) {
+    static_cast<__bf16*>(base)[i] = static_cast<__bf16>(x);  // round to nearest even
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// One iteration of a lane group's online softmax over U key rows
+// (rows r0, r0 + RSTEP, ...).  MASK handles the ragged last iteration: rows at
+// or beyond ke get score -inf and their (clamped, in-bounds) loads are unused.
+template <int DT, int LPR, int RSTEP, int U, int ROWB, bool MASK, int NH>
+__device__ __forceinline__ void online_step(const char* kp, const char* vp, const uint4 (&qv)[NH],
+                                            int r0, int ke, float sl2, float (&m)[NH],
+                                            float (&l)[NH],
+                                            float (&o)[NH][Elem<DT>::VEC]) {
+  using E = Elem<DT>;
+  constexpr int VEC = E::VEC;
+  uint4 kr[U], vr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
+    kr[u] = ld16(kp + static_cast<size_t>(r) * ROWB);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
+    vr[u] = ld16(vp + static_cast<size_t>(r) * ROWB);
+  }
+  float s[NH][U];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    float mc = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x = group_sum<LPR>(E::dot(qv[j], kr[u])) * sl2;
+      if (MASK && r0 + u * RSTEP >= ke) x = kNegInf;
+      s[j][u] = x;
+      mc = fmaxf(mc, x);
+    }
+    if (mc > m[j] + kRescaleSlack) {
+      const float alpha = exp2_hw(m[j] - mc);  // 0 on the first update (m = -inf)
+      l[j] *= alpha;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[j][i] *= alpha;
+      m[j] = mc;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float vf[VEC];
+    E::widen(vr[u], vf);
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      // A lane group that has seen only masked rows still has m = -inf.
+      const float mu = MASK ? (m[j] == kNegInf ? 0.f : m[j]) : m[j];
+      const float p = exp2_hw(s[j][u] - mu);
+      l[j] += p;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[j][i] = fmaf(p, vf[i], o[j][i]);
+    }
+  }
+}
+
+// Merge the (m, l, o) streams of the lane groups of one wave (xor butterfly
+// over the group index).
+template <int LPR, int VEC, int NH>
+__device__ __forceinline__ void merge_wave(float (&m)[NH], float (&l)[NH], float (&o)[NH][VEC]) {
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const float m2 = __shfl_xor(m[j], off);
+      const float l2 = __shfl_xor(l[j], off);
+      const float M = fmaxf(m[j], m2);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      const float a1 = exp2_hw(m[j] - Mu), a2 = exp2_hw(m2 - Mu);
+      l[j] = a1 * l[j] + a2 * l2;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[j][i] = a1 * o[j][i] + a2 * __shfl_xor(o[j][i], off);
+      m[j] = M;
+    }
+  }
+}
+
+// Shared body of the head kernel (NH = 1) and the group kernel (NH heads of
+// one KV group).  heads[j] < 0 marks an unused head slot of the last chunk.
+template <int DT, int D, int WAVES, int U, int NH>
+__device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, int b, int g,
+                                            const int (&heads)[NH], int part_head0,
+                                            int part_heads) {
+  using E = Elem<DT>;
+  constexpr int VEC = E::VEC;
+  constexpr int ES = 16 / VEC;            // bytes per element
+  constexpr int ROWB = D * ES;            // bytes per key row
+  constexpr int LPR = D / VEC;            // lanes per key row
+  constexpr int RPW = 64 / LPR;           // rows per wave per load
+  constexpr int RSTEP = WAVES * RPW;      // rows per unroll step (whole workgroup)
+  constexpr int RITER = RSTEP * U;        // rows per iteration
+
+  __shared__ float sm_o[WAVES][NH][D];
+  __shared__ float sm_ml[WAVES][NH][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / LPR, sub = lane % LPR;
+
+  const int ks = split * a.chunk;
+  const int ke = min(ks + a.chunk, a.Nkv);
+
+  const size_t kv_off =
+      ((static_cast<size_t>(b) * a.H_kv + g) * static_cast<size_t>(a.Nkv)) * D + sub * VEC;
+  const char* kp = static_cast<const char*>(a.k) + kv_off * ES;
+  const char* vp = static_cast<const char*>(a.v) + kv_off * ES;
+
+  uint4 qv[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    qv[j] = make_uint4(0, 0, 0, 0);
+    if (heads[j] >= 0)
+      qv[j] = ld16(static_cast<const char*>(a.q) +
+                   ((static_cast<size_t>(b) * a.H + heads[j]) * D + sub * VEC) * ES);
+  }
+
+  float m[NH], l[NH], o[NH][VEC];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[j][i] = 0.f;
+  }
+
+  const int lrow = wave * RPW + grp;
+  int base = ks;
+  const int nfull = (ke - ks) / RITER;
+  for (int it = 0; it < nfull; ++it, base += RITER)
+    online_step<DT, LPR, RSTEP, U, ROWB, false, NH>(kp, vp, qv, base + lrow, ke, a.scale_log2, m, l, o);
+  if (base < ke)
+    online_step<DT, LPR, RSTEP, U, ROWB, true, NH>(kp, vp, qv, base + lrow, ke, a.scale_log2, m, l, o);
+
+  merge_wave<LPR, VEC, NH>(m, l, o);
+
+  if (grp == 0) {
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) sm_o[wave][j][sub * VEC + i] = o[j][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      sm_ml[wave][j][0] = m[j];
+      sm_ml[wave][j][1] = l[j];
+    }
+  }
+  __syncthreads();
+
+  // Merge across waves: one output element per thread.
+  for (int e = tid; e < NH * D; e += WAVES * 64) {
+    const int j = e / D, c = e % D;
+    if (heads[j] < 0) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_ml[w][j][0]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float wt = exp2_hw(sm_ml[w][j][0] - Mu);
+      L += wt * sm_ml[w][j][1];
+      acc += wt * sm_o[w][j][c];
+    }
+    if (a.nsplit == 1) {
+      E::store(a.o, (static_cast<size_t>(b) * a.H + heads[j]) * D + c, acc / L);
+    } else {
+      const size_t p = (static_cast<size_t>(unit) * part_heads + part_head0 + j) * a.nsplit + split;
+      a.part_o[p * D + c] = acc;
+      if (c == 0) {
+        a.part_ml[2 * p] = M;
+        a.part_ml[2 * p + 1] = L;
+      }
+    }
+  }
+}
+
+// Head-indexed unit: blockIdx.x = unit * nsplit + split.
+template <int DT, int D, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void sha_decode_mha_kernel(Args a) {
+  const int split = blockIdx.x % a.nsplit;
+  const int unit = blockIdx.x / a.nsplit;
+  const int h = a.idx[unit];
+  if (h < 0 || h >= a.H) return;  // padding / out-of-range entry: no read, no write
+  const int heads[1] = {h};
+  decode_unit<DT, D, WAVES, U, 1>(a, unit, split, unit / a.top_k, h / a.G, heads, 0, 1);
+}
+
+// Group-indexed unit: blockIdx.x = (unit * nchunk + chunk) * nsplit + split;
+// the workgroup computes query heads g*G + chunk*NH + j of group g.
+template <int DT, int D, int WAVES, int U, int NH>
+__global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_kernel(Args a) {
+  const int nchunk = (a.G + NH - 1) / NH;
+  const int split = blockIdx.x % a.nsplit;
+  const int rest = blockIdx.x / a.nsplit;
+  const int chunk = rest % nchunk;
+  const int unit = rest / nchunk;
+  const int g = a.idx[unit];
+  if (g < 0 || g >= a.H_kv) return;
+  int heads[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const int hj = chunk * NH + j;
+    heads[j] = (hj < a.G) ? g * a.G + hj : -1;
+  }
+  decode_unit<DT, D, WAVES, U, NH>(a, unit, split, unit / a.top_k, g, heads, chunk * NH, a.G);
+}
+
+// Merge the nsplit partials of one (unit, head): blockIdx.x = unit *
+// heads_per_unit + j, one thread per output element, fixed split order.
+template <int DT, int D>
+__global__ __launch_bounds__(D) void sha_combine_kernel(Args a, int gqa) {
+  const int hpu = gqa ? a.G : 1;
+  const int unit = blockIdx.x / hpu, j = blockIdx.x % hpu;
+  const int id = a.idx[unit];
+  int h;
+  if (gqa) {
+    if (id < 0 || id >= a.H_kv) return;
+    h = id * a.G + j;
+  } else {
+    if (id < 0 || id >= a.H) return;
+    h = id;
+  }
+  const int c = threadIdx.x;
+  const size_t p0 = static_cast<size_t>(blockIdx.x) * a.nsplit;
+  float M = kNegInf;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (p0 + s)]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float wt = exp2_hw(a.part_ml[2 * (p0 + s)] - Mu);
+    L += wt * a.part_ml[2 * (p0 + s) + 1];
+    acc += wt * a.part_o[(p0 + s) * D + c];
+  }
+  Elem<DT>::store(a.o, (static_cast<size_t>(unit / a.top_k) * a.H + h) * D + c, acc / L);
+}
+
+// ---------------------------------------------------------------------------
+// Launch variants: (waves per workgroup, rows per lane group per iteration).
+// Variant 0 is the default; the others exist for tuning sweeps.
+// ---------------------------------------------------------------------------
+constexpr KernelShape kMhaShapes[] = {{4, 4}, {4, 2}, {4, 8}, {8, 2}, {8, 4}, {2, 8}, {1, 8}, {2, 4}};
+constexpr int kNumMha = sizeof(kMhaShapes) / sizeof(kMhaShapes[0]);
+constexpr KernelShape kGqaShapes[] = {{4, 2}, {4, 1}, {2, 2}, {8, 1}, {4, 4}};
+constexpr int kNumGqa = sizeof(kGqaShapes) / sizeof(kGqaShapes[0]);
+
+template <int DT, int D>
+hipError_t launch_combine(const Args& a, int gqa, hipStream_t st) {
+  const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * (gqa ? a.G : 1);
+  hipLaunchKernelGGL((sha_combine_kernel<DT, D>), dim3(blocks), dim3(D), 0, st, a, gqa);
+  return hipGetLastError();
+}
+
+template <int DT, int D, int V>
+hipError_t launch_mha_v(const Args& a, hipStream_t st) {
+  constexpr KernelShape s = kMhaShapes[V];
+  const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * a.nsplit;
+  hipLaunchKernelGGL((sha_decode_mha_kernel<DT, D, s.waves, s.unroll>), dim3(blocks),
+                     dim3(s.waves * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.nsplit > 1) e = launch_combine<DT, D>(a, 0, st);
+  return e;
+}
+
+template <int DT, int D, int V, int NH>
+hipError_t launch_gqa_v(const Args& a, hipStream_t st) {
+  constexpr KernelShape s = kGqaShapes[V];
+  const unsigned nchunk = (a.G + NH - 1) / NH;
+  const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * nchunk * a.nsplit;
+  hipLaunchKernelGGL((sha_decode_gqa_kernel<DT, D, s.waves, s.unroll, NH>), dim3(blocks),
+                     dim3(s.waves * 64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.nsplit > 1) e = launch_combine<DT, D>(a, 1, st);
+  return e;
+}
+
+template <int DT, int D>
+hipError_t launch_mha_d(const Args& a, int variant, hipStream_t st) {
+  switch (variant) {
+    case 1: return launch_mha_v<DT, D, 1>(a, st);
+    case 2: return launch_mha_v<DT, D, 2>(a, st);
+    case 3: return launch_mha_v<DT, D, 3>(a, st);
+    case 4: return launch_mha_v<DT, D, 4>(a, st);
+    case 5: return launch_mha_v<DT, D, 5>(a, st);
+    case 6: return launch_mha_v<DT, D, 6>(a, st);
+    case 7: return launch_mha_v<DT, D, 7>(a, st);
+    default: return launch_mha_v<DT, D, 0>(a, st);
+  }
+}
+
+template <int DT, int D, int NH>
+hipError_t launch_gqa_nh(const Args& a, int variant, hipStream_t st) {
+  switch (variant) {
+    case 1: return launch_gqa_v<DT, D, 1, NH>(a, st);
+    case 2: return launch_gqa_v<DT, D, 2, NH>(a, st);
+    case 3: return launch_gqa_v<DT, D, 3, NH>(a, st);
+    case 4: return launch_gqa_v<DT, D, 4, NH>(a, st);
+    default: return launch_gqa_v<DT, D, 0, NH>(a, st);
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_gqa_d(const Args& a, int variant, hipStream_t st) {
+  switch (gqa_heads_per_wg(a.G)) {
+    case 2: return launch_gqa_nh<DT, D, 2>(a, variant, st);
+    case 4: return launch_gqa_nh<DT, D, 4>(a, variant, st);
+    default: return launch_gqa_nh<DT, D, 8>(a, variant, st);
+  }
+}
+
+template <int DT>
+hipError_t launch_mha_dt(const Args& a, int d, int variant, hipStream_t st) {
+  return d == 64 ? launch_mha_d<DT, 64>(a, variant, st) : launch_mha_d<DT, 128>(a, variant, st);
+}
+
+template <int DT>
+hipError_t launch_gqa_dt(const Args& a, int d, int variant, hipStream_t st) {
+  return d == 64 ? launch_gqa_d<DT, 64>(a, variant, st) : launch_gqa_d<DT, 128>(a, variant, st);
+}
+
+int clamp_variant(int v, int n) { return (v < 0 || v >= n) ? 0 : v; }
+
+}  // namespace
+
+KernelShape mha_shape(int, int, int variant) { return kMhaShapes[clamp_variant(variant, kNumMha)]; }
+KernelShape gqa_shape(int, int, int variant) { return kGqaShapes[clamp_variant(variant, kNumGqa)]; }
+
+int gqa_heads_per_wg(int G) { return G <= 2 ? 2 : (G <= 4 ? 4 : 8); }
+
+hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t st) {
+  variant = clamp_variant(variant, kNumMha);
+  switch (dtype) {
+    case kF32: return launch_mha_dt<kF32>(a, d, variant, st);
+    case kF16: return launch_mha_dt<kF16>(a, d, variant, st);
+    default: return launch_mha_dt<kBF16>(a, d, variant, st);
+  }
+}
+
+hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, hipStream_t st) {
+  variant = clamp_variant(variant, kNumGqa);
+  switch (dtype) {
+    case kF32: return launch_gqa_dt<kF32>(a, d, variant, st);
+    case kF16: return launch_gqa_dt<kF16>(a, d, variant, st);
+    default: return launch_gqa_dt<kBF16>(a, d, variant, st);
+  }
+}
+
+}  // namespace sha

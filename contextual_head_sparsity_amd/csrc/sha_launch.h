@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (sha_api.cpp) and the HIP kernels
+// (sha_kernels.hip).  Not installed; callers use include/sha.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace sha {
+
+// Everything a launch needs, validated by the host before it gets here.
+struct Args {
+  const void* q;        // [B, H, 1, d]
+  const void* k;        // [B, H_kv, Nkv, d]
+  const void* v;        // [B, H_kv, Nkv, d]
+  const int32_t* idx;   // [B, top_k]: head ids (MHA) or group ids (GQA)
+  void* o;              // [B, H, 1, d]
+  float* part_o;        // split partials: [units * heads_per_unit * nsplit, d] (unnormalised)
+  float* part_ml;       // split partials: [units * heads_per_unit * nsplit, 2] = (m, l), log2 domain
+  int B, H, H_kv, Nkv, top_k;
+  int G;                // H / H_kv
+  int nsplit;           // effective split count (every split holds >= 1 key)
+  int chunk;            // keys per split (last split may hold fewer)
+  float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
+};
+
+enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Kernel shape of the split kernel: waves per workgroup and keys per lane
+// group per iteration.  Exposed so the planner can size splits to it.
+struct KernelShape {
+  int waves;
+  int unroll;
+};
+
+KernelShape mha_shape(int dtype, int d, int variant);
+KernelShape gqa_shape(int dtype, int d, int variant);
+// Query heads one GQA workgroup computes (<= 8); a group of G heads takes
+// ceil(G / gqa_heads_per_wg(G)) workgroups per split.
+int gqa_heads_per_wg(int G);
+
+hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t stream);
+hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, hipStream_t stream);
+
+}  // namespace sha

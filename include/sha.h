@@ -1,0 +1,184 @@
+/*
+ * sha.h - C ABI of the Selective Head Attention (SHA) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch row b and every slot k of an index
+ * tensor, one decode-attention pass of a single query vector over all Nkv
+ * keys of its head:
+ *
+ *     O[b, h, 0, :] = softmax(scale * q K^T) V,   q = Q[b, h, 0, :],
+ *                     K = K[b, g, :, :], V = V[b, g, :, :]
+ *
+ * Definition: Polar Sparsity notes (papernotes.org), section 方法详解 >
+ * 关键设计 > "Attention Head 稀疏性" (per-head softmax(Q K^T / sqrt(d_h)) V).
+ * Selection: the same notes, "Selective Head Attention (SHA) Kernel" (the
+ * kernel takes a batch head index tensor, one thread-block per batch row and
+ * head, only active heads are read and written, GQA models use group
+ * sparsity), and the Polar Sparsity reproducibility page (ri.k117.org),
+ * "Pseudocode", Algorithm 1 "Selective Head Flash Attention (Decode)": a unit
+ * (b, k) resolves head_idx = batch_head_index[b, k] (steps 1-2), streams K/V
+ * of that head in tiles with a running max / running sum softmax (steps
+ * 3-10) and writes O[b, head_idx, 0, :] (step 11).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; they must
+ *     stay valid until the work queued on `stream` has finished.  The library
+ *     keeps no caller pointer after a call returns.
+ *   - Layouts are contiguous row-major:
+ *         q, o : [B, H, 1, d]          (H = number of query heads)
+ *         k, v : [B, H_kv, Nkv, d]
+ *         index: [B, top_k] int32
+ *     q, k, v and o share one element type (dtype); accumulation is fp32,
+ *     the result is rounded to the element type (round to nearest even).
+ *   - d must be 64 or 128 (else SHA_ERR_UNSUPPORTED).  q, k, v, o and a
+ *     workspace must be 16-byte aligned, the index 4-byte aligned (else
+ *     SHA_ERR_MISALIGNED).
+ *   - B == 0 or top_k == 0 is an empty call: nothing is read or written and
+ *     SHA_OK is returned (null pointers are then allowed).  Nkv must be >= 1
+ *     (a softmax over no keys is undefined).
+ *   - Output slots [b, h] that no index entry selects are never written: a
+ *     caller that needs zeros there zeroes o first.
+ *   - An index entry outside [0, H) (head entry points) or [0, H_kv) (group
+ *     entry points), for example -1 used as padding, is skipped: that unit
+ *     reads and writes nothing.  Duplicate entries compute the same slot
+ *     twice with identical bits.  Index contents are device data and are not
+ *     checked on the host (that would need a device synchronisation).
+ *   - Calls are asynchronous: they validate on the host, enqueue on `stream`
+ *     and return.  Scalar/pointer errors are returned before anything is
+ *     enqueued; a failing launch returns SHA_ERR_HIP (the raw hipError_t is
+ *     available from sha_last_hip_error()); device faults surface at the
+ *     caller's next synchronisation.
+ *   - Results are deterministic: no atomics, fixed reduction order.  The
+ *     split count (see sha_decode_ex) changes the rounding order, so results
+ *     are bitwise reproducible for a fixed split count.
+ */
+#ifndef SHA_H_
+#define SHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SHA_F32 = 0, SHA_F16 = 1, SHA_BF16 = 2 } sha_dtype;
+
+typedef enum {
+  SHA_OK = 0,
+  SHA_ERR_INVALID_ARG = 1,  /* bad scalar (negative size, H % H_kv != 0, top_k out of range, Nkv < 1, non-finite scale) or null pointer */
+  SHA_ERR_UNSUPPORTED = 2,  /* head dimension other than 64 / 128, unknown dtype, group size > 64 */
+  SHA_ERR_MISALIGNED = 3,   /* pointer alignment below what the 128-bit loads need */
+  SHA_ERR_WORKSPACE = 4,    /* workspace null or smaller than sha_workspace_bytes() */
+  SHA_ERR_HIP = 5           /* a HIP runtime call or launch failed */
+} sha_status;
+
+/*
+ * Head-indexed SHA decode (the Algorithm 1 unit: one query head per index
+ * entry).  batch_head_index[b, k] names a query head in [0, H).  With
+ * H_kv < H (H % H_kv == 0, G = H / H_kv) head h reads KV head h / G.
+ *   scale : score scale, normally 1/sqrt(d) (Algorithm 1's s); must be finite.
+ *   stream: HIP stream to enqueue on (0 = the null stream).
+ * The library picks the split count and uses an internal, per-device cached
+ * workspace when it needs one (allocated on first need, grown, kept until
+ * the process ends; calls from several host threads are serialised around
+ * it).  Callers that must not allocate use sha_decode_ex.
+ * The three typed forms take exactly these arguments; sha_decode adds dtype.
+ */
+sha_status sha_decode_f32(const void* q, const void* k, const void* v,
+                          const int32_t* batch_head_index, int B, int H, int H_kv,
+                          int Nkv, int d, int top_k, float scale, void* o,
+                          hipStream_t stream);
+sha_status sha_decode_f16(const void* q, const void* k, const void* v,
+                          const int32_t* batch_head_index, int B, int H, int H_kv,
+                          int Nkv, int d, int top_k, float scale, void* o,
+                          hipStream_t stream);
+sha_status sha_decode_bf16(const void* q, const void* k, const void* v,
+                           const int32_t* batch_head_index, int B, int H, int H_kv,
+                           int Nkv, int d, int top_k, float scale, void* o,
+                           hipStream_t stream);
+sha_status sha_decode(const void* q, const void* k, const void* v,
+                      const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                      int d, int top_k, float scale, void* o, hipStream_t stream,
+                      sha_dtype dtype);
+
+/*
+ * Group-indexed SHA decode (GQA group sparsity).  batch_group_index[b, k]
+ * names a KV group g in [0, H_kv); all G = H / H_kv query heads
+ * g*G .. g*G+G-1 of the group are computed against K/V[b, g], which is
+ * streamed once per unit and shared by the G heads.  top_k counts groups
+ * (1 <= top_k <= H_kv).  G may be 1..64.  Other arguments as sha_decode.
+ * Group sparsity: Polar Sparsity notes (papernotes.org), SHA Kernel bullet on
+ * GQA; atlas.scime.ai summary, "Approach" (routers pick top-k heads or GQA
+ * groups).  The contiguous head-to-group numbering is the usual grouped-query
+ * layout (the pages do not spell it out).
+ */
+sha_status sha_decode_gqa_f32(const void* q, const void* k, const void* v,
+                              const int32_t* batch_group_index, int B, int H, int H_kv,
+                              int Nkv, int d, int top_k, float scale, void* o,
+                              hipStream_t stream);
+sha_status sha_decode_gqa_f16(const void* q, const void* k, const void* v,
+                              const int32_t* batch_group_index, int B, int H, int H_kv,
+                              int Nkv, int d, int top_k, float scale, void* o,
+                              hipStream_t stream);
+sha_status sha_decode_gqa_bf16(const void* q, const void* k, const void* v,
+                               const int32_t* batch_group_index, int B, int H, int H_kv,
+                               int Nkv, int d, int top_k, float scale, void* o,
+                               hipStream_t stream);
+sha_status sha_decode_gqa(const void* q, const void* k, const void* v,
+                          const int32_t* batch_group_index, int B, int H, int H_kv,
+                          int Nkv, int d, int top_k, float scale, void* o,
+                          hipStream_t stream, sha_dtype dtype);
+
+/*
+ * Explicit-workspace forms: no allocation inside the call.
+ *   nsplit   : number of KV splits per unit (flash-decoding split-K); 0 lets
+ *              the library choose (sha_plan_nsplit).  Values above Nkv are
+ *              clamped.  With an effective split count above 1 the call runs
+ *              the split kernel and then a combine kernel that merges the
+ *              per-split (o, m, l) partials with the same running-max rule
+ *              as Algorithm 1 step 8.
+ *   workspace: device buffer of at least sha_workspace_bytes(...) bytes for
+ *              the same arguments (may be null when that is 0), owned by the
+ *              caller; its contents on entry do not matter.  Calls that
+ *              share one workspace must be ordered (same stream).
+ */
+sha_status sha_decode_ex(const void* q, const void* k, const void* v,
+                         const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                         int d, int top_k, float scale, void* o, hipStream_t stream,
+                         sha_dtype dtype, int nsplit, void* workspace, size_t workspace_bytes);
+sha_status sha_decode_gqa_ex(const void* q, const void* k, const void* v,
+                             const int32_t* batch_group_index, int B, int H, int H_kv,
+                             int Nkv, int d, int top_k, float scale, void* o,
+                             hipStream_t stream, sha_dtype dtype, int nsplit,
+                             void* workspace, size_t workspace_bytes);
+
+/*
+ * Launch planning (host only, no device work).
+ *   sha_plan_nsplit    : the split count the library would use; num_cus <= 0
+ *                        queries the current device's compute-unit count.
+ *                        Returns a value >= 1, or 0 for invalid arguments.
+ *   sha_workspace_bytes: workspace bytes needed for nsplit (0 = planned
+ *                        split count, same num_cus rule); 0 when no
+ *                        workspace is needed.  gqa != 0 selects the group
+ *                        entry points' accounting.
+ */
+int sha_plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
+                    sha_dtype dtype, int num_cus);
+size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
+                           sha_dtype dtype, int nsplit, int num_cus);
+
+/* Human-readable name of a status code (static storage). */
+const char* sha_status_string(sha_status s);
+/* Raw hipError_t of the last SHA_ERR_HIP returned on the calling thread. */
+int sha_last_hip_error(void);
+/* Library version, "major.minor.patch" (static storage). */
+const char* sha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHA_H_ */

@@ -1,0 +1,81 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+and compare with the fp64 oracle element by element."""
+import numpy as np
+import torch
+
+import contextual_head_sparsity_amd as sha
+from contextual_head_sparsity_amd import workloads as wl
+from oracle import sha_decode_gqa_ref, sha_decode_ref, sha_units_ref
+
+# Max abs error on active heads for N(0, 1) inputs, per element type.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+TOL_T = {torch.float32: 1e-5, torch.float16: 2e-3, torch.bfloat16: 1e-2}
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(gqa, q, k, v, idx, scale, o, nsplit=0, workspace=None):
+    fn = sha.sha_decode_gqa if gqa else sha.sha_decode
+    fn(q, k, v, idx, scale=scale, out=o, nsplit=nsplit, workspace=workspace)
+    torch.cuda.synchronize()
+    return o
+
+
+def check_full(gqa, q, k, v, idx, scale, o_before, o_after, tol):
+    """Whole-call comparison: every slot, with the oracle on the CPU."""
+    ref_fn = sha_decode_gqa_ref if gqa else sha_decode_ref
+    ref, written = ref_fn(q.cpu(), k.cpu(), v.cpu(), idx.cpu(), scale)
+    got = o_after.cpu()
+    g64 = got.to(torch.float64).numpy()
+    w = written
+    assert np.isfinite(g64[w]).all(), "non-finite output in an active slot"
+    err = float(np.max(np.abs(g64[w] - ref[w]))) if w.any() else 0.0
+    assert err <= tol, f"max abs error {err:.3e} > {tol}"
+    wt = torch.from_numpy(w)
+    assert torch.equal(wl.raw_bits(got)[~wt], wl.raw_bits(o_before.cpu())[~wt]), \
+        "an inactive slot changed"
+    return err, written
+
+
+def written_mask(idx_cpu: np.ndarray, H: int, H_kv: int, gqa: bool) -> np.ndarray:
+    B = idx_cpu.shape[0]
+    G = H // H_kv
+    w = np.zeros((B, H), bool)
+    for b in range(B):
+        for e in idx_cpu[b]:
+            if gqa:
+                if 0 <= e < H_kv:
+                    w[b, e * G:(e + 1) * G] = True
+            elif 0 <= e < H:
+                w[b, e] = True
+    return w
+
+
+def check_sampled(gqa, q, k, v, idx, scale, o_before_bits, o_after, tol, n_samples, seed):
+    """Full-size comparison: a seeded sample of active (b, h) slots against the
+    oracle computed unit by unit, plus whole-tensor properties (every active
+    slot finite, every inactive slot bit-identical to its prefill)."""
+    B, H = q.shape[:2]
+    H_kv = k.shape[1]
+    G = H // H_kv
+    idx_cpu = idx.cpu().numpy()
+    w = written_mask(idx_cpu, H, H_kv, gqa)
+    wt = torch.from_numpy(w).to(o_after.device)
+    bits = wl.raw_bits(o_after)
+    assert torch.equal(bits[~wt], o_before_bits[~wt]), "an inactive slot changed"
+    assert torch.isfinite(o_after[wt]).all(), "non-finite output in an active slot"
+    rng = np.random.default_rng(seed)
+    active = np.argwhere(w)
+    pick = active[rng.choice(len(active), size=min(n_samples, len(active)), replace=False)]
+    qs = torch.stack([q[b, h, 0] for b, h in pick]).cpu()
+    ks = torch.stack([k[b, h // G] for b, h in pick]).cpu()
+    vs = torch.stack([v[b, h // G] for b, h in pick]).cpu()
+    ref = sha_units_ref(qs, ks, vs, scale)
+    got = torch.stack([o_after[b, h, 0] for b, h in pick]).cpu().to(torch.float64).numpy()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= tol, f"max abs error {err:.3e} > {tol} on sampled slots"
+    return err

@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from contextual_head_sparsity_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sha.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bd.LIB_PATH),
+                                reason="libsha.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sha_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    names = _declared_functions()
+    assert len(names) == 15, names
+    L = ctypes.CDLL(bd.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert set(names) == set(bd.SIGNATURES), "binding and header disagree"
+    bd.lib()
+
+
+def test_status_strings_and_version():
+    L = bd.lib()
+    for code, name in bd.STATUS.items():
+        assert L.sha_status_string(code).decode() == name
+    assert re.fullmatch(r"\d+\.\d+\.\d+", L.sha_version().decode())
+
+
+A16 = 0x10000       # a fake, 16-byte aligned "device" address: never dereferenced
+ARGS = dict(B=2, H=4, H_kv=4, Nkv=64, d=64, top_k=2)
+
+
+def _decode(fn="sha_decode_ex", q=A16, k=A16, v=A16, idx=A16, o=A16, scale=0.125, dtype=0,
+            nsplit=1, ws=None, ws_bytes=0, **kw):
+    a = dict(ARGS, **kw)
+    L = bd.lib()
+    base = (q, k, v, idx, a["B"], a["H"], a["H_kv"], a["Nkv"], a["d"], a["top_k"], scale, o, None)
+    if fn in ("sha_decode_ex", "sha_decode_gqa_ex"):
+        return getattr(L, fn)(*base, dtype, nsplit, ws, ws_bytes)
+    if fn in ("sha_decode", "sha_decode_gqa"):
+        return getattr(L, fn)(*base, dtype)
+    return getattr(L, fn)(*base)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Nkv=0), 1), (dict(B=-1), 1), (dict(top_k=-1), 1), (dict(H=4, H_kv=3), 1),
+    (dict(top_k=5), 1), (dict(H_kv=0), 1), (dict(d=96), 2), (dict(d=256), 2), (dict(dtype=7), 2),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(idx=None), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1), (dict(k=A16 + 8), 3), (dict(o=A16 + 2), 3), (dict(idx=A16 + 2), 3),
+    (dict(nsplit=-1), 1),
+])
+def test_host_validation_errors(kw, expect):
+    assert _decode(**kw) == expect
+
+
+def test_empty_calls_are_noops():
+    # B == 0 or top_k == 0: nothing to read or write, null pointers allowed.
+    assert _decode(B=0, q=None, k=None, v=None, idx=None, o=None) == 0
+    assert _decode(top_k=0, q=None, k=None, v=None, idx=None, o=None) == 0
+    assert _decode(fn="sha_decode_gqa_ex", top_k=0, H=8, H_kv=2, q=None, k=None, v=None,
+                   idx=None, o=None) == 0
+
+
+def test_gqa_validation():
+    assert _decode(fn="sha_decode_gqa_ex", H=8, H_kv=2, top_k=3) == 1   # top_k > H_kv
+    assert _decode(fn="sha_decode_gqa_ex", H=130, H_kv=2, top_k=1) == 2  # group of 65 heads
+
+
+def test_typed_entry_points_validate():
+    for fn in ("sha_decode_f32", "sha_decode_f16", "sha_decode_bf16", "sha_decode_gqa_f32",
+               "sha_decode_gqa_f16", "sha_decode_gqa_bf16", "sha_decode", "sha_decode_gqa"):
+        assert _decode(fn=fn, Nkv=0) == 1
+        assert _decode(fn=fn, d=80) == 2
+
+
+def test_workspace_errors():
+    # A split call needs a workspace: missing or short -> SHA_ERR_WORKSPACE.
+    need = bd.lib().sha_workspace_bytes(2, 4, 4, 64, 64, 2, 0, 0, 4, 256)
+    assert need > 0
+    assert _decode(nsplit=4) == 4
+    assert _decode(nsplit=4, ws=A16, ws_bytes=need - 1) == 4
+    assert _decode(nsplit=4, ws=A16 + 4, ws_bytes=need) == 3
+
+
+def test_planner_and_workspace_accounting():
+    L = bd.lib()
+    # OPT-66B layer: 1408 units already give every CU several workgroups.
+    assert L.sha_plan_nsplit(64, 72, 72, 1920, 128, 22, 0, 1, 256) == 1
+    # A small grid (256 units) is split along the keys to fill 256 CUs.
+    ns = L.sha_plan_nsplit(16, 32, 32, 1024, 128, 16, 0, 1, 256)
+    assert ns > 1
+    # Workspace: per (unit, head, split) d fp32 partial outputs + (m, l).
+    ws = L.sha_workspace_bytes(16, 32, 32, 1024, 128, 16, 0, 1, ns, 256)
+    n = 16 * 16 * ns
+    assert ws == (n * 128 * 4 + 255) // 256 * 256 + n * 8
+    assert L.sha_workspace_bytes(16, 32, 32, 1024, 128, 16, 0, 1, 1, 256) == 0
+    # GQA accounting counts every query head of a group.
+    n = 64 * 5 * 8 * 3
+    assert L.sha_workspace_bytes(64, 64, 8, 8192, 128, 5, 1, 2, 3, 256) == \
+        (n * 128 * 4 + 255) // 256 * 256 + n * 8
+    # Split count never exceeds Nkv, invalid arguments plan to 0.
+    assert L.sha_plan_nsplit(1, 4, 4, 1, 64, 1, 0, 0, 256) == 1
+    assert L.sha_plan_nsplit(1, 4, 4, 0, 64, 1, 0, 0, 256) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 1, 64)
+    k = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        bd.sha_decode(q, k, k, torch.zeros(1, 1, dtype=torch.int32))
