@@ -43,10 +43,11 @@ def build(verbose: bool = True) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    kern = os.path.join(objdir, "sha_kernels.o")
-    _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
-          os.path.join(CSRC, "sha_kernels.hip"), "-o", kern])
-    objs.append(kern)
+    for src in ("sha_kernels.hip", "sha_gqa_mfma.hip"):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
+              os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
     api = os.path.join(objdir, "sha_api.o")
     _run([hipcc, "-c", *COMMON, os.path.join(CSRC, "sha_api.cpp"), "-o", api])
     objs.append(api)

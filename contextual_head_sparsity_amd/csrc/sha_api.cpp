@@ -69,13 +69,19 @@ int gqa_variant() {
   static const int v = env_int("SHA_GQA_VARIANT", 0);
   return v;
 }
+// Group calls in f16 / bf16 run on the matrix cores; SHA_GQA_VALU=1 selects
+// the vector-ALU kernel instead (for comparisons).
+bool gqa_mfma(int dtype) {
+  static const bool force_valu = env_int("SHA_GQA_VALU", 0) != 0;
+  return dtype != SHA_F32 && !force_valu;
+}
 
 // Workgroups one split of the whole call launches.
-long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa) {
+long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa, int dtype) {
   long long per_unit = 1;
   if (gqa) {
     const int G = H / H_kv;
-    const int nh = sha::gqa_heads_per_wg(G);
+    const int nh = sha::gqa_heads_per_wg(G, gqa_mfma(dtype));
     per_unit = G == 1 ? 1 : (G + nh - 1) / nh;
   }
   return static_cast<long long>(B) * top_k * per_unit;
@@ -85,6 +91,7 @@ long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa) {
 // steps); splits are sized in whole iterations where possible.
 int rows_per_iter(int d, int dtype, int gqa, int H, int H_kv) {
   const bool use_gqa = gqa && H / H_kv > 1;
+  if (use_gqa && gqa_mfma(dtype)) return sha::gqa_mfma_keys_per_iter();
   const sha::KernelShape s =
       use_gqa ? sha::gqa_shape(dtype, d, gqa_variant()) : sha::mha_shape(dtype, d, mha_variant());
   const int vec = dtype == SHA_F32 ? 4 : 8;
@@ -97,7 +104,7 @@ int rows_per_iter(int d, int dtype, int gqa, int H, int H_kv) {
 // shorter than two iterations of the split kernel.
 int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
                 int num_cus) {
-  const long long wgs = wgs_per_split(B, H, H_kv, top_k, gqa);
+  const long long wgs = wgs_per_split(B, H, H_kv, top_k, gqa, dtype);
   if (wgs <= 0) return 1;
   const long long target = 4LL * device_cus(num_cus);
   long long ns = (target + wgs - 1) / wgs;
@@ -198,7 +205,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   split_geometry(p.Nkv, req, &ns, &chunk);
 
   // Grid limit: blocks * threads per block (at most 512) must fit 32 bits.
-  const long long blocks = wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa) * ns;
+  const long long blocks = wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa, p.dtype) * ns;
   if (blocks > (1LL << 23)) return SHA_ERR_INVALID_ARG;
 
   sha::Args a{};
@@ -229,7 +236,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   }
 
   (void)hipGetLastError();  // do not report an earlier, unrelated error as ours
-  const hipError_t e = gqa_eff ? sha::launch_gqa(a, p.dtype, p.d, gqa_variant(), stream)
+  const hipError_t e = gqa_eff ? sha::launch_gqa(a, p.dtype, p.d, gqa_variant(), gqa_mfma(p.dtype), stream)
                                : sha::launch_mha(a, p.dtype, p.d, mha_variant(), stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;

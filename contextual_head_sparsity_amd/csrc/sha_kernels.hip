@@ -34,112 +34,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sha_device.h"
 #include "sha_launch.h"
 
 namespace sha {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
-// Lazy-rescale slack in base-2 units: probabilities are bounded by 2^8.
-constexpr float kRescaleSlack = 8.0f;
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of LPR lanes; every lane of the group receives
-// the same total.
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(LPR == 8 || LPR == 16 || LPR == 32, "lanes per key row");
-  x += dpp<0xB1>(x);                               // quad_perm [1,0,3,2]
-  x += dpp<0x4E>(x);                               // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);                              // row_half_mirror (8 lanes)
-  if constexpr (LPR >= 16) x += dpp<0x140>(x);     // row_mirror (16 lanes)
-  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
-  return x;
-}
-
-// Element types: 16 bytes per lane per load.
-template <int DT>
-struct Elem;
-
-template <>
-struct Elem<kF32> {
-  static constexpr int VEC = 4;
-  __device__ static float dot(uint4 q, uint4 k) {
-    float s = __uint_as_float(q.x) * __uint_as_float(k.x);
-    s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
-    s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
-    return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
-  }
-  __device__ static void widen(uint4 v, float* f) {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
-  }
-  __device__ static void store(void* base, size_t i, float x) { static_cast<float*>(base)[i] = x; }
-};
-
-template <>
-struct Elem<kF16> {
-  static constexpr int VEC = 8;
-  __device__ static float dot(uint4 q, uint4 k) {
-    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.x), __builtin_bit_cast(h2_t, k.x), 0.f, false);
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.y), __builtin_bit_cast(h2_t, k.y), s, false);
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.z), __builtin_bit_cast(h2_t, k.z), s, false);
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q.w), __builtin_bit_cast(h2_t, k.w), s, false);
-  }
-  __device__ static void widen2(uint32_t w, float* f) {
-    const h2_t h = __builtin_bit_cast(h2_t, w);
-    f[0] = static_cast<float>(h.x);
-    f[1] = static_cast<float>(h.y);
-  }
-  __device__ static void widen(uint4 v, float* f) {
-    widen2(v.x, f);
-    widen2(v.y, f + 2);
-    widen2(v.z, f + 4);
-    widen2(v.w, f + 6);
-  }
-  __device__ static void store(void* base, size_t i, float x) {
-    static_cast<_Float16*>(base)[i] = static_cast<_Float16>(x);
-  }
-};
-
-template <>
-struct Elem<kBF16> {
-  static constexpr int VEC = 8;
-  __device__ static float dot(uint4 q, uint4 k) {
-    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.x), __builtin_bit_cast(b2_t, k.x), 0.f, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.y), __builtin_bit_cast(b2_t, k.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.z), __builtin_bit_cast(b2_t, k.z), s, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q.w), __builtin_bit_cast(b2_t, k.w), s, false);
-  }
-  // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
-  __device__ static void widen2(uint32_t w, float* f) {
-    f[0] = __uint_as_float(w << 16);
-    f[1] = __uint_as_float(w & 0xFFFF0000u);
-  }
-  __device__ static void widen(uint4 v, float* f) {
-    widen2(v.x, f);
-    widen2(v.y, f + 2);
-    widen2(v.z, f + 4);
-    widen2(v.w, f + 6);
-  }
-  __device__ static void store(void* base, size_t i, float x) {
-    static_cast<__bf16*>(base)[i] = static_cast<__bf16>(x);  // round to nearest even
-  }
-};
-
-__device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+using namespace detail;
 
 // One iteration of a lane group's online softmax over U key rows
 // (rows r0, r0 + RSTEP, ...).  MASK handles the ragged last iteration: rows at
@@ -389,7 +290,7 @@ constexpr KernelShape kGqaShapes[] = {{4, 2}, {4, 1}, {2, 2}, {8, 1}, {4, 4}};
 constexpr int kNumGqa = sizeof(kGqaShapes) / sizeof(kGqaShapes[0]);
 
 template <int DT, int D>
-hipError_t launch_combine(const Args& a, int gqa, hipStream_t st) {
+hipError_t launch_combine_t(const Args& a, int gqa, hipStream_t st) {
   const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * (gqa ? a.G : 1);
   hipLaunchKernelGGL((sha_combine_kernel<DT, D>), dim3(blocks), dim3(D), 0, st, a, gqa);
   return hipGetLastError();
@@ -402,7 +303,7 @@ hipError_t launch_mha_v(const Args& a, hipStream_t st) {
   hipLaunchKernelGGL((sha_decode_mha_kernel<DT, D, s.waves, s.unroll>), dim3(blocks),
                      dim3(s.waves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && a.nsplit > 1) e = launch_combine<DT, D>(a, 0, st);
+  if (e == hipSuccess && a.nsplit > 1) e = launch_combine_t<DT, D>(a, 0, st);
   return e;
 }
 
@@ -414,7 +315,7 @@ hipError_t launch_gqa_v(const Args& a, hipStream_t st) {
   hipLaunchKernelGGL((sha_decode_gqa_kernel<DT, D, s.waves, s.unroll, NH>), dim3(blocks),
                      dim3(s.waves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e == hipSuccess && a.nsplit > 1) e = launch_combine<DT, D>(a, 1, st);
+  if (e == hipSuccess && a.nsplit > 1) e = launch_combine_t<DT, D>(a, 1, st);
   return e;
 }
 
@@ -445,7 +346,7 @@ hipError_t launch_gqa_nh(const Args& a, int variant, hipStream_t st) {
 
 template <int DT, int D>
 hipError_t launch_gqa_d(const Args& a, int variant, hipStream_t st) {
-  switch (gqa_heads_per_wg(a.G)) {
+  switch (gqa_heads_per_wg(a.G, false)) {
     case 2: return launch_gqa_nh<DT, D, 2>(a, variant, st);
     case 4: return launch_gqa_nh<DT, D, 4>(a, variant, st);
     default: return launch_gqa_nh<DT, D, 8>(a, variant, st);
@@ -469,7 +370,20 @@ int clamp_variant(int v, int n) { return (v < 0 || v >= n) ? 0 : v; }
 KernelShape mha_shape(int, int, int variant) { return kMhaShapes[clamp_variant(variant, kNumMha)]; }
 KernelShape gqa_shape(int, int, int variant) { return kGqaShapes[clamp_variant(variant, kNumGqa)]; }
 
-int gqa_heads_per_wg(int G) { return G <= 2 ? 2 : (G <= 4 ? 4 : 8); }
+int gqa_heads_per_wg(int G, bool mfma) {
+  if (mfma) return 16;
+  return G <= 2 ? 2 : (G <= 4 ? 4 : 8);
+}
+
+int gqa_mfma_keys_per_iter() { return 4 * 32; }
+
+hipError_t launch_combine(const Args& a, int dtype, int d, int gqa, hipStream_t st) {
+  switch (dtype) {
+    case kF32: return d == 64 ? launch_combine_t<kF32, 64>(a, gqa, st) : launch_combine_t<kF32, 128>(a, gqa, st);
+    case kF16: return d == 64 ? launch_combine_t<kF16, 64>(a, gqa, st) : launch_combine_t<kF16, 128>(a, gqa, st);
+    default: return d == 64 ? launch_combine_t<kBF16, 64>(a, gqa, st) : launch_combine_t<kBF16, 128>(a, gqa, st);
+  }
+}
 
 hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t st) {
   variant = clamp_variant(variant, kNumMha);
@@ -480,7 +394,8 @@ hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t 
   }
 }
 
-hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, hipStream_t st) {
+hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, bool mfma, hipStream_t st) {
+  if (mfma && dtype != kF32) return launch_gqa_mfma(a, dtype, d, st);
   variant = clamp_variant(variant, kNumGqa);
   switch (dtype) {
     case kF32: return launch_gqa_dt<kF32>(a, d, variant, st);

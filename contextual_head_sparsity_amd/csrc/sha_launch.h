@@ -36,11 +36,19 @@ struct KernelShape {
 
 KernelShape mha_shape(int dtype, int d, int variant);
 KernelShape gqa_shape(int dtype, int d, int variant);
-// Query heads one GQA workgroup computes (<= 8); a group of G heads takes
-// ceil(G / gqa_heads_per_wg(G)) workgroups per split.
-int gqa_heads_per_wg(int G);
+// Query heads one GQA workgroup computes: 16 on the matrix-core path (one
+// MFMA column per head), <= 8 on the vector path; a group of G heads takes
+// ceil(G / gqa_heads_per_wg(...)) workgroups per split.
+int gqa_heads_per_wg(int G, bool mfma);
+// Keys one workgroup iteration of the matrix-core GQA kernel consumes.
+int gqa_mfma_keys_per_iter();
 
 hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t stream);
-hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, hipStream_t stream);
+// Vector-ALU GQA kernel (any dtype) or, with mfma, the matrix-core kernel
+// (f16 / bf16 only).
+hipError_t launch_gqa(const Args& a, int dtype, int d, int variant, bool mfma, hipStream_t stream);
+hipError_t launch_gqa_mfma(const Args& a, int dtype, int d, hipStream_t stream);
+// Split merge for nsplit > 1 (gqa != 0: every head of each selected group).
+hipError_t launch_combine(const Args& a, int dtype, int d, int gqa, hipStream_t stream);
 
 }  // namespace sha
