@@ -33,12 +33,19 @@ import contextual_head_sparsity_amd as sha  # noqa: E402
 from contextual_head_sparsity_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
-KERNEL_SRC = os.path.join(ROOT, "contextual_head_sparsity_amd", "csrc", "sha_kernels.hip")
+CSRC = os.path.join(ROOT, "contextual_head_sparsity_amd", "csrc")
+KERNEL_SOURCES = ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_device.h", "sha_launch.h")
+METRIC = "SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), OPT-66B shape B=64"
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the device sources: counter-derived traffic is only reported
+    for the kernels it was measured on."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -54,6 +61,13 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calib", action="store_true")
+    p.add_argument("--summarize-traffic", action="store_true",
+                   help="write profiles/traffic_<workload>.json from rocprofv3 --pmc CSVs")
+    p.add_argument("--fetch-csv")
+    p.add_argument("--write-csv")
+    p.add_argument("--copy-fetch-csv")
+    p.add_argument("--copy-write-csv")
+    p.add_argument("--grid", type=int, default=0, help="decode dispatch grid size to select")
     return p.parse_args()
 
 
@@ -70,20 +84,25 @@ def copy_calib(steps: int):
 
 
 def time_calls(call, steps: int, warmup: int, stream):
-    """Wall time of `steps` back-to-back calls, and per-call HIP-event
-    durations recorded on the launch stream."""
+    """Time `steps` back-to-back calls twice: once bracketed only by device
+    synchronisation (wall time per call, the throughput figure), once with a
+    HIP event pair around every call on the launch stream (per-launch kernel
+    durations for the roofline)."""
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
         call(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return wall / steps * 1e3, ev_ms
 
@@ -123,8 +142,12 @@ def cpu_baseline(w, q, k, v, idx, budget_s: float):
                       f"{spent:.1f} s timed, {per_call * 1e6:.0f} us per layer call"}
 
 
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
 def load_traffic(workload: str):
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -134,8 +157,59 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(csv_path: str, counter: str):
+    import csv
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                yield row
+
+
+def summarize_traffic(args):
+    """Turn rocprofv3 --pmc CSVs (FETCH_SIZE / WRITE_SIZE, KiB per dispatch)
+    into HBM bytes per decode launch, each counter scaled by what it reads
+    for a device copy of known size in the same kind of run."""
+    w = wl.WORKLOADS[args.workload]
+    kname = "sha_decode_gqa_mfma_kernel" if w.gqa else "sha_decode_mha_kernel"
+
+    def avg(csv_path, counter, match, grid=None):
+        vals = [float(r["Counter_Value"]) for r in _counter_rows(csv_path, counter)
+                if match(r["Kernel_Name"]) and (grid is None or int(r["Grid_Size"]) == grid)]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel in {csv_path}")
+        return sum(vals) / len(vals), len(vals)
+
+    grid = args.grid or None
+    is_dec = lambda n: kname in n
+    is_copy = lambda n: "copy" in n.lower() and "sha" not in n
+    f_dec, nf = avg(args.fetch_csv, "FETCH_SIZE", is_dec, grid)
+    w_dec, nw = avg(args.write_csv, "WRITE_SIZE", is_dec, grid)
+    f_cp, _ = avg(args.copy_fetch_csv, "FETCH_SIZE", is_copy)
+    w_cp, _ = avg(args.copy_write_csv, "WRITE_SIZE", is_copy)
+    copy_bytes = float(1 << 30)
+    fetch_scale = copy_bytes / (f_cp * 1024)
+    write_scale = copy_bytes / (w_cp * 1024)
+    read_b = f_dec * 1024 * fetch_scale
+    write_b = w_dec * 1024 * write_scale
+    rec = {"workload": w.name, "kernel": kname, "kernel_source_sha256_16": kernel_hash(),
+           "dispatches": {"fetch": nf, "write": nw},
+           "fetch_size_kib_per_launch": f_dec, "write_size_kib_per_launch": w_dec,
+           "copy_1GiB_fetch_kib": f_cp, "copy_1GiB_write_kib": w_cp,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+           "hbm_bytes_per_launch": read_b + write_b,
+           "algorithmic_bytes_per_launch": w.active_kv_bytes,
+           "ratio_to_algorithmic": (read_b + write_b) / w.active_kv_bytes}
+    with open(traffic_path(w.name), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: SHA decode units are independent and this "
               "build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
@@ -196,7 +270,8 @@ def main():
     achieved = w.active_kv_bytes / (ev_avg_ms / 1e3) / 1e9
     traffic = load_traffic(w.name)
     out = {
-        "metric": "SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), OPT-66B shape B=64",
+        "metric": METRIC if w.name == wl.HEADLINE else
+                  f"SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), {w.name}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -217,7 +292,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "sha_decode_gqa_kernel" if w.gqa else "sha_decode_mha_kernel",
+                     "kernel": "sha_decode_gqa_mfma_kernel" if w.gqa else "sha_decode_mha_kernel",
                      "launch_avg_us": round(ev_avg_ms * 1e3, 2),
                      "launch_p10_us": round(float(np.percentile(ev, 10)) * 1e3, 2),
                      "launch_p90_us": round(float(np.percentile(ev, 90)) * 1e3, 2),

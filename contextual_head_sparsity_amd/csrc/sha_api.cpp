@@ -87,30 +87,27 @@ long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa, int dtype) {
   return static_cast<long long>(B) * top_k * per_unit;
 }
 
-// Keys one iteration of a workgroup consumes (all lane groups, all unroll
-// steps); splits are sized in whole iterations where possible.
-int rows_per_iter(int d, int dtype, int gqa, int H, int H_kv) {
-  const bool use_gqa = gqa && H / H_kv > 1;
-  if (use_gqa && gqa_mfma(dtype)) return sha::gqa_mfma_keys_per_iter();
-  const sha::KernelShape s =
-      use_gqa ? sha::gqa_shape(dtype, d, gqa_variant()) : sha::mha_shape(dtype, d, mha_variant());
-  const int vec = dtype == SHA_F32 ? 4 : 8;
-  const int rows_per_wave = 64 / (d / vec);
-  return s.waves * rows_per_wave * s.unroll;
-}
+// Split count (flash-decoding split-K over the keys), from measurements on
+// MI355X: a head-indexed workgroup (4 waves, 16 KiB of loads in flight per
+// wave) streams ~22 GB/s, so about one workgroup per CU saturates HBM and
+// splitting further only adds partials and tail; the matrix-core group
+// kernel holds 2 workgroups per CU and has a serial load -> MFMA -> LDS ->
+// MFMA chain per tile, and does best with about four workgroups per CU.
+// No split is shorter than kMinSplitKeys keys.
+constexpr int kMinSplitKeys = 512;
+constexpr int kMaxSplits = 64;
 
-// Split count: enough workgroups to give every CU several (the grid must be
-// much larger than 256 CUs to fill the chip and hide the tail), but no split
-// shorter than two iterations of the split kernel.
 int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
                 int num_cus) {
+  (void)d;
   const long long wgs = wgs_per_split(B, H, H_kv, top_k, gqa, dtype);
   if (wgs <= 0) return 1;
-  const long long target = 4LL * device_cus(num_cus);
+  const bool mfma = gqa && H / H_kv > 1 && gqa_mfma(dtype);
+  const long long target = (mfma ? 4LL : 1LL) * device_cus(num_cus);
   long long ns = (target + wgs - 1) / wgs;
-  const int min_rows = 2 * rows_per_iter(d, dtype, gqa, H, H_kv);
-  const long long max_ns = Nkv / min_rows > 1 ? Nkv / min_rows : 1;
+  const long long max_ns = Nkv / kMinSplitKeys > 1 ? Nkv / kMinSplitKeys : 1;
   if (ns > max_ns) ns = max_ns;
+  if (ns > kMaxSplits) ns = kMaxSplits;
   if (ns < 1) ns = 1;
   const int env = env_int("SHA_NSPLIT", 0);
   if (env > 0) ns = env;

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
       if (!full) row = min(row, ke - 1);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kr[mb][kc] = ld16(kbase + static_cast<size_t>(row) * ROWB + kc * 64 + q4 * 16);
+        kr[mb][kc] = ld16_stream(kbase + static_cast<size_t>(row) * ROWB + kc * 64 + q4 * 16);
     }
     // V tile: 1 KiB contiguous per wave load.
     uint4 vr[VLD];
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
     for (int u = 0; u < VLD; ++u) {
       int row = base + u * (1024 / ROWB) + lane / LPRW;
       if (!full) row = min(row, ke - 1);
-      vr[u] = ld16(vbase + static_cast<size_t>(row) * ROWB + (lane % LPRW) * 16);
+      vr[u] = ld16_stream(vbase + static_cast<size_t>(row) * ROWB + (lane % LPRW) * 16);
     }
 
     // Scores S^T = K Q^T: lane holds keys 16*mb + 4*q4 + r of head col.

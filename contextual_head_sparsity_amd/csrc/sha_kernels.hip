@@ -56,12 +56,12 @@ __device__ __forceinline__ void online_step(const char* kp, const char* vp, cons
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
-    kr[u] = ld16(kp + static_cast<size_t>(r) * ROWB);
+    kr[u] = ld16_stream(kp + static_cast<size_t>(r) * ROWB);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
-    vr[u] = ld16(vp + static_cast<size_t>(r) * ROWB);
+    vr[u] = ld16_stream(vp + static_cast<size_t>(r) * ROWB);
   }
   float s[NH][U];
 #pragma unroll
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(D) void sha_combine_kernel(Args a, int gqa) {
 // Launch variants: (waves per workgroup, rows per lane group per iteration).
 // Variant 0 is the default; the others exist for tuning sweeps.
 // ---------------------------------------------------------------------------
-constexpr KernelShape kMhaShapes[] = {{4, 4}, {4, 2}, {4, 8}, {8, 2}, {8, 4}, {2, 8}, {1, 8}, {2, 4}};
+constexpr KernelShape kMhaShapes[] = {{4, 8}, {4, 4}, {4, 2}, {8, 2}, {8, 4}, {2, 8}, {1, 8}, {2, 4}};
 constexpr int kNumMha = sizeof(kMhaShapes) / sizeof(kMhaShapes[0]);
 constexpr KernelShape kGqaShapes[] = {{4, 2}, {4, 1}, {2, 2}, {8, 1}, {4, 4}};
 constexpr int kNumGqa = sizeof(kGqaShapes) / sizeof(kGqaShapes[0]);
@@ -367,15 +367,12 @@ int clamp_variant(int v, int n) { return (v < 0 || v >= n) ? 0 : v; }
 
 }  // namespace
 
-KernelShape mha_shape(int, int, int variant) { return kMhaShapes[clamp_variant(variant, kNumMha)]; }
-KernelShape gqa_shape(int, int, int variant) { return kGqaShapes[clamp_variant(variant, kNumGqa)]; }
 
 int gqa_heads_per_wg(int G, bool mfma) {
   if (mfma) return 16;
   return G <= 2 ? 2 : (G <= 4 ? 4 : 8);
 }
 
-int gqa_mfma_keys_per_iter() { return 4 * 32; }
 
 hipError_t launch_combine(const Args& a, int dtype, int d, int gqa, hipStream_t st) {
   switch (dtype) {

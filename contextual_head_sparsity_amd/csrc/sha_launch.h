@@ -27,21 +27,17 @@ struct Args {
 
 enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
-// Kernel shape of the split kernel: waves per workgroup and keys per lane
-// group per iteration.  Exposed so the planner can size splits to it.
+// Shape of a vector-ALU split kernel: waves per workgroup and key rows per
+// lane group per iteration.
 struct KernelShape {
   int waves;
   int unroll;
 };
 
-KernelShape mha_shape(int dtype, int d, int variant);
-KernelShape gqa_shape(int dtype, int d, int variant);
 // Query heads one GQA workgroup computes: 16 on the matrix-core path (one
 // MFMA column per head), <= 8 on the vector path; a group of G heads takes
 // ceil(G / gqa_heads_per_wg(...)) workgroups per split.
 int gqa_heads_per_wg(int G, bool mfma);
-// Keys one workgroup iteration of the matrix-core GQA kernel consumes.
-int gqa_mfma_keys_per_iter();
 
 hipError_t launch_mha(const Args& a, int dtype, int d, int variant, hipStream_t stream);
 // Vector-ALU GQA kernel (any dtype) or, with mfma, the matrix-core kernel

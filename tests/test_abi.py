@@ -96,14 +96,19 @@ def test_workspace_errors():
 
 def test_planner_and_workspace_accounting():
     L = bd.lib()
-    # OPT-66B layer: 1408 units already give every CU several workgroups.
+    # Head-indexed: about one workgroup per CU.  The OPT-66B layer (1408
+    # units) and a 256-unit layer need no split; 64 units split 4 ways; a
+    # single short row is capped so that no split is shorter than 512 keys.
     assert L.sha_plan_nsplit(64, 72, 72, 1920, 128, 22, 0, 1, 256) == 1
-    # A small grid (256 units) is split along the keys to fill 256 CUs.
-    ns = L.sha_plan_nsplit(16, 32, 32, 1024, 128, 16, 0, 1, 256)
-    assert ns > 1
+    assert L.sha_plan_nsplit(16, 32, 32, 1024, 128, 16, 0, 1, 256) == 1
+    assert L.sha_plan_nsplit(4, 32, 32, 4096, 128, 16, 0, 1, 256) == 4
+    assert L.sha_plan_nsplit(1, 32, 32, 4096, 128, 16, 0, 1, 256) == 8
+    # Group (matrix-core) kernel: about four workgroups per CU.
+    assert L.sha_plan_nsplit(64, 64, 8, 8192, 128, 5, 1, 2, 256) == 4
     # Workspace: per (unit, head, split) d fp32 partial outputs + (m, l).
-    ws = L.sha_workspace_bytes(16, 32, 32, 1024, 128, 16, 0, 1, ns, 256)
-    n = 16 * 16 * ns
+    ns = 4
+    ws = L.sha_workspace_bytes(4, 32, 32, 4096, 128, 16, 0, 1, 0, 256)
+    n = 4 * 16 * ns
     assert ws == (n * 128 * 4 + 255) // 256 * 256 + n * 8
     assert L.sha_workspace_bytes(16, 32, 32, 1024, 128, 16, 0, 1, 1, 256) == 0
     # GQA accounting counts every query head of a group.
