@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--copy-fetch-csv")
     p.add_argument("--copy-write-csv")
     p.add_argument("--grid", type=int, default=0, help="decode dispatch grid size to select")
+    p.add_argument("--mlp", default=None, choices=list(wl.MLP_WORKLOADS),
+                   help="measure the selective MLP on this workload instead of SHA decode")
+    p.add_argument("--mlp-batch", type=int, default=0, help="override the MLP workload's B")
     return p.parse_args()
 
 
@@ -205,8 +208,71 @@ def summarize_traffic(args):
     print(json.dumps(rec))
 
 
+def bench_mlp(args):
+    """Selective MLP (device union + up/down projections) on one GPU: time per
+    layer call and effective GB/s on the selected neurons' weight rows."""
+    w = wl.MLP_WORKLOADS[args.mlp]
+    if args.mlp_batch:
+        w = w.with_(B=args.mlp_batch)
+    dev = torch.device("cuda:0")
+    x, w1t, w2t, rows = wl.make_mlp(w, dev)
+    copies = 2
+    ws = [(w1t, w2t)]
+    for c in range(1, copies):
+        ws.append((torch.roll(w1t, c, 0).contiguous(), torch.roll(w2t, c, 0).contiguous()))
+    stream = torch.cuda.current_stream(dev)
+    sel = torch.empty(min(w.D, w.B * w.k_row), dtype=torch.int32, device=dev)
+    n_sel = torch.empty(1, dtype=torch.int32, device=dev)
+    n_max = sel.numel()
+    wsb = sha.selective_mlp_workspace_bytes(w.B, w.d, w.D, n_max)
+    work = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    uws = torch.empty(w.D + 256, dtype=torch.uint8, device=dev)
+    sha.mlp_union(rows, w.D, sel=sel, n_sel=n_sel, workspace=uws)
+    torch.cuda.synchronize()
+    n = int(n_sel.item())
+
+    def call(i):
+        sha.mlp_union(rows, w.D, sel=sel, n_sel=n_sel, stream=stream, workspace=uws)
+        a, b = ws[i % copies]
+        sha.selective_mlp(x, a, b, sel, n_sel, n_max=n_max, out=y, workspace=work, stream=stream)
+
+    ms, ev = time_calls(call, args.steps, args.warmup, stream)
+    sel_all = torch.arange(w.D, dtype=torch.int32, device=dev)
+    n_all = torch.tensor([w.D], dtype=torch.int32, device=dev)
+    wsd = torch.empty(max(sha.selective_mlp_workspace_bytes(w.B, w.d, w.D, w.D), 1),
+                      dtype=torch.uint8, device=dev)
+
+    def dcall(i):
+        a, b = ws[i % copies]
+        sha.selective_mlp(x, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd, stream=stream)
+
+    dms, _ = time_calls(dcall, args.steps, args.warmup, stream)
+    wbytes = n * w.weight_bytes_per_neuron
+    out = {"metric": f"selective MLP \u00b5s/layer + effective weight GB/s, {w.name}",
+           "value": round(wbytes / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
+           "us_per_layer": round(ms * 1e3, 2),
+           "pct_hbm_peak": round(100 * wbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+           "dtype": w.dtype, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "config": {"workload": w.name, "B": w.B, "d": w.d, "D": w.D, "k_row": w.k_row,
+                      "union": n, "union_frac": round(n / w.D, 4), "weight_bytes": wbytes},
+           "roofline": {"bound": "hbm", "achieved": round(wbytes / (float(np.mean(ev)) / 1e3) / 1e9, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(wbytes / (float(np.mean(ev)) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "launch_avg_us": round(float(np.mean(ev)) * 1e3, 2),
+                        "note": "event span covers union + up + down (+ finalize) kernels"},
+           "all_neurons": {"us_per_layer": round(dms * 1e3, 2),
+                           "GBps": round(w.D * w.weight_bytes_per_neuron / (dms / 1e3) / 1e9, 2),
+                           "speedup_selective_vs_all": round(dms / ms, 3),
+                           "ideal_speedup": round(w.D / max(n, 1), 3)}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.mlp:
+        bench_mlp(args)
+        return
     if args.summarize_traffic:
         summarize_traffic(args)
         return

@@ -37,6 +37,10 @@ SIGNATURES = {
     "sha_decode_gqa_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
     "sha_plan_nsplit": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "sha_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "sha_mlp_union_workspace_bytes": (_S, [_I]),
+    "sha_mlp_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _S]),
+    "sha_selective_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "sha_selective_mlp": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _S]),
     "sha_status_string": (ctypes.c_char_p, [_I]),
     "sha_last_hip_error": (_I, []),
     "sha_version": (ctypes.c_char_p, []),
@@ -151,3 +155,82 @@ def sha_decode_gqa(q, k, v, batch_group_index, scale=None, out=None, nsplit=0, w
                    stream=None):
     """Group-indexed (GQA group sparsity) SHA decode; see sha_decode."""
     return _call(True, q, k, v, batch_group_index, scale, out, nsplit, workspace, stream)
+
+
+# ---------------------------------------------------------------------------
+# selective MLP
+# ---------------------------------------------------------------------------
+
+def _dev_i32(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != torch.int32:
+        t = t.to(torch.int32)
+    return t.contiguous()
+
+
+def mlp_union(row_neurons, D, sel=None, n_sel=None, stream=None, workspace=None):
+    """Sorted union of the rows' neuron lists (entries outside [0, D) skipped),
+    on the device: returns (sel [min(D, B*k)] int32, n_sel [1] int32)."""
+    rows = _dev_i32(row_neurons, "row_neurons")
+    if rows.dim() != 2:
+        raise ValueError("row_neurons must be [B, k]")
+    B, k = rows.shape
+    cap = max(1, min(D, B * k))
+    if sel is None:
+        sel = torch.empty(cap, dtype=torch.int32, device=rows.device)
+    elif sel.numel() < cap or sel.dtype != torch.int32 or not sel.is_contiguous():
+        raise ValueError(f"sel must be a contiguous int32 tensor of >= {cap} entries")
+    if n_sel is None:
+        n_sel = torch.empty(1, dtype=torch.int32, device=rows.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(rows.device)
+    need = lib().sha_mlp_union_workspace_bytes(D)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
+    with torch.cuda.device(rows.device):
+        st = lib().sha_mlp_union(rows.data_ptr(), B, k, D, sel.data_ptr(), n_sel.data_ptr(),
+                                 stream.cuda_stream, workspace.data_ptr(), need)
+    _check(st, "sha_mlp_union")
+    return sel, n_sel
+
+
+def selective_mlp_workspace_bytes(B, d, D, n_max, num_cus=0) -> int:
+    return lib().sha_selective_mlp_workspace_bytes(B, d, D, n_max, num_cus)
+
+
+def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None, stream=None):
+    """y = relu(x w1t[S]^T) w2t[S], S = sel[:n_sel] (device count).
+
+    x [B, d]; w1t, w2t [D, d] (neuron-major: W1^T and W2^T); f16 or bf16.
+    n_max bounds the count (default: sel.numel()).
+    """
+    for name, t in (("x", x), ("w1t", w1t), ("w2t", w2t)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D device tensor")
+    if x.dtype not in (torch.float16, torch.bfloat16) or w1t.dtype != x.dtype or w2t.dtype != x.dtype:
+        raise ValueError("x, w1t, w2t must share float16 or bfloat16")
+    B, d = x.shape
+    D = w1t.shape[0]
+    if w1t.shape != (D, d) or w2t.shape != (D, d):
+        raise ValueError("w1t and w2t must be [D, d]")
+    sel = _dev_i32(sel, "sel")
+    n_sel = _dev_i32(n_sel, "n_sel")
+    if n_max is None:
+        n_max = min(sel.numel(), D)
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    L = lib()
+    need = L.sha_selective_mlp_workspace_bytes(B, d, D, n_max, 0)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = L.sha_selective_mlp(x.data_ptr(), w1t.data_ptr(), w2t.data_ptr(), sel.data_ptr(),
+                                 n_sel.data_ptr(), n_max, B, d, D, out.data_ptr(),
+                                 stream.cuda_stream, _DT[x.dtype], workspace.data_ptr(), need)
+    _check(st, "sha_selective_mlp")
+    return out

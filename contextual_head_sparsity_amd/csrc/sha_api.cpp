@@ -242,6 +242,55 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   return SHA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// selective MLP planning
+// ---------------------------------------------------------------------------
+struct MlpPlan {
+  int n_pad, b_pad, up_splits, up_kper, dn_splits;
+  size_t h_bytes, up_bytes, dn_bytes;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Grid sizes from the selection bound: the up projection has one workgroup
+// per 64 selected neurons x 64 batch rows and splits its K (d) when that is
+// fewer than two workgroups per CU; the down projection has one workgroup
+// per 256 output columns x 64 rows and splits the neuron range until it has
+// about one workgroup per CU (each split range keeps >= 64 neurons).
+MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
+  MlpPlan p{};
+  const int cus = device_cus(num_cus);
+  p.n_pad = ((n_max > 0 ? n_max : 1) + 63) / 64 * 64;
+  p.b_pad = (B + 63) / 64 * 64;
+  const long long up_wgs = static_cast<long long>(p.n_pad / 64) * (p.b_pad / 64);
+  long long us = (2LL * cus + up_wgs - 1) / up_wgs;
+  const int kchunks = d / 256;
+  if (us > kchunks) us = kchunks;
+  if (us > 64) us = 64;
+  if (us < 1) us = 1;
+  p.up_kper = (kchunks + static_cast<int>(us) - 1) / static_cast<int>(us) * 256;
+  p.up_splits = (d + p.up_kper - 1) / p.up_kper;
+  const long long dn_wgs = static_cast<long long>(d / 256) * (p.b_pad / 64);
+  long long ds = (static_cast<long long>(cus) + dn_wgs - 1) / dn_wgs;
+  const long long ds_max = n_max / 64 > 1 ? n_max / 64 : 1;
+  if (ds > ds_max) ds = ds_max;
+  if (ds > 64) ds = 64;
+  if (ds < 1) ds = 1;
+  p.dn_splits = static_cast<int>(ds);
+  p.h_bytes = round256(static_cast<size_t>(p.b_pad) * p.n_pad * 2);
+  p.up_bytes = p.up_splits > 1 ? round256(static_cast<size_t>(p.up_splits) * p.b_pad * p.n_pad * 4) : 0;
+  p.dn_bytes = p.dn_splits > 1 ? round256(static_cast<size_t>(p.dn_splits) * p.b_pad * d * 4) : 0;
+  return p;
+}
+
+sha_status check_mlp(int B, int d, int D, int n_max, int dtype) {
+  if (B < 0 || d < 1 || D < 1 || n_max < 0 || n_max > D) return SHA_ERR_INVALID_ARG;
+  if (dtype != SHA_F16 && dtype != SHA_BF16) return SHA_ERR_UNSUPPORTED;
+  if (d % 256 != 0) return SHA_ERR_UNSUPPORTED;
+  if (B > 65535 * 64) return SHA_ERR_INVALID_ARG;
+  return SHA_OK;
+}
+
 Problem make(const void* q, const void* k, const void* v, const int32_t* idx, int B, int H,
              int H_kv, int Nkv, int d, int top_k, float scale, void* o, int dtype, bool gqa) {
   return Problem{q, k, v, idx, o, B, H, H_kv, Nkv, d, top_k, scale, dtype, gqa};
@@ -347,6 +396,80 @@ size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, in
   int ns = 1, chunk = Nkv;
   split_geometry(Nkv, req, &ns, &chunk);
   return partial_bytes(B, H, H_kv, d, top_k, gqa && H / H_kv > 1, ns);
+}
+
+size_t sha_mlp_union_workspace_bytes(int D) {
+  return D < 1 ? 0 : round256(static_cast<size_t>(D));
+}
+
+sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_t* sel,
+                         int32_t* n_sel, hipStream_t stream, void* workspace,
+                         size_t workspace_bytes) {
+  if (B < 0 || k < 0 || D < 1) return SHA_ERR_INVALID_ARG;
+  const long long total = static_cast<long long>(B) * k;
+  if (total > 0x7FFFFFFFLL) return SHA_ERR_INVALID_ARG;
+  if (!sel || !n_sel || (total > 0 && !row_neurons)) return SHA_ERR_INVALID_ARG;
+  if (!aligned(sel, 4) || !aligned(n_sel, 4) || (row_neurons && !aligned(row_neurons, 4)))
+    return SHA_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < sha_mlp_union_workspace_bytes(D)) return SHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  const hipError_t e = sha::launch_mlp_union(row_neurons, static_cast<int>(total), D, sel, n_sel,
+                                             static_cast<uint8_t*>(workspace), stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return SHA_ERR_HIP;
+  }
+  return SHA_OK;
+}
+
+size_t sha_selective_mlp_workspace_bytes(int B, int d, int D, int n_max, int num_cus) {
+  if (check_mlp(B, d, D, n_max, SHA_BF16) != SHA_OK || B == 0) return 0;
+  const MlpPlan p = mlp_plan(B, d, n_max, num_cus);
+  return p.h_bytes + p.up_bytes + p.dn_bytes;
+}
+
+sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, const int32_t* sel,
+                             const int32_t* n_sel, int n_max, int B, int d, int D, void* y,
+                             hipStream_t stream, sha_dtype dtype, void* workspace,
+                             size_t workspace_bytes) {
+  const sha_status st = check_mlp(B, d, D, n_max, dtype);
+  if (st != SHA_OK || B == 0) return st;
+  if (!x || !w1t || !w2t || !sel || !n_sel || !y) return SHA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1t, 16) || !aligned(w2t, 16) || !aligned(y, 16) ||
+      !aligned(sel, 4) || !aligned(n_sel, 4))
+    return SHA_ERR_MISALIGNED;
+  const MlpPlan p = mlp_plan(B, d, n_max, 0);
+  const size_t need = p.h_bytes + p.up_bytes + p.dn_bytes;
+  if (!workspace || workspace_bytes < need) return SHA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
+  sha::MlpArgs a{};
+  a.x = x;
+  a.w1t = w1t;
+  a.w2t = w2t;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.y = y;
+  char* ws = static_cast<char*>(workspace);
+  a.h = ws;
+  a.up_part = p.up_bytes ? reinterpret_cast<float*>(ws + p.h_bytes) : nullptr;
+  a.dn_part = p.dn_bytes ? reinterpret_cast<float*>(ws + p.h_bytes + p.up_bytes) : nullptr;
+  a.B = B;
+  a.d = d;
+  a.D = D;
+  a.n_max = n_max;
+  a.n_pad = p.n_pad;
+  a.b_pad = p.b_pad;
+  a.up_splits = p.up_splits;
+  a.up_kper = p.up_kper;
+  a.dn_splits = p.dn_splits;
+  (void)hipGetLastError();
+  const hipError_t e = sha::launch_selective_mlp(a, dtype, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return SHA_ERR_HIP;
+  }
+  return SHA_OK;
 }
 
 const char* sha_status_string(sha_status s) {

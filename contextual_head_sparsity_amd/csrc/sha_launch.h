@@ -47,4 +47,27 @@ hipError_t launch_gqa_mfma(const Args& a, int dtype, int d, hipStream_t stream);
 // Split merge for nsplit > 1 (gqa != 0: every head of each selected group).
 hipError_t launch_combine(const Args& a, int dtype, int d, int gqa, hipStream_t stream);
 
+// Selective MLP (batch union of active neurons).  Sizes validated on the host;
+// the selection count is device data, clamped to n_max by the kernels.
+struct MlpArgs {
+  const void* x;        // [B, d]
+  const void* w1t;      // [D, d]  (W1^T, neuron-major)
+  const void* w2t;      // [D, d]  (W2^T, neuron-major)
+  const int32_t* sel;   // [>= n_max] selected neurons; entries outside [0, D) contribute nothing
+  const int32_t* n_sel; // device count of valid leading entries of sel
+  void* y;              // [B, d]
+  void* h;              // workspace: relu(x W1[:, S]), [b_pad, n_pad] 16-bit
+  float* up_part;       // workspace: up-projection K-split partials [up_splits, b_pad, n_pad]
+  float* dn_part;       // workspace: down-projection split partials [dn_splits, b_pad, d]
+  int B, d, D, n_max;
+  int n_pad, b_pad;     // n_max rounded up to 64, B rounded up to 64
+  int up_splits, up_kper;  // K splits of the up projection and K elements per split
+  int dn_splits;        // neuron-range splits of the down projection
+};
+
+// flags: workspace of round_up(D, 256) bytes.
+hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
+                            uint8_t* flags, hipStream_t stream);
+hipError_t launch_selective_mlp(const MlpArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace sha

@@ -1,0 +1,500 @@
+// Selective MLP ("Selective GEMM") of Polar Sparsity on gfx950.
+//
+// papernotes.org notes on Polar Sparsity, 方法详解 > 关键设计 > "MLP 层动态稀疏":
+// for a decode batch x [B, d], MLP_{S_B}(x) = sigma(x W1[:, S_B]) W2[:, S_B]^T
+// where S_B is the union over the batch of every row's active neurons, and
+// the indexing is fused into the matrix products (no gather/scatter pass).
+// sigma is ReLU (the selective MLP is applied to OPT models).  Weights are
+// stored neuron-major: w1t = W1^T and w2t = W2^T, both [D, d], so a selected
+// neuron is one contiguous row of each.
+//
+// Kernels:
+//   union  - a flag byte per neuron in a workspace: cleared, marked by every
+//            row's entries (plain byte stores, any order gives the same flags),
+//            then one workgroup scans the flags and writes the marked neurons
+//            in ascending order and their count, on device (deterministic).
+//   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
+//            a workgroup owns 64 selected neurons x 64 batch rows; the
+//            selected weight rows stream from HBM straight into A operands
+//            (non-temporal 128-bit loads, one K chunk prefetched ahead), the
+//            x chunk is staged once per workgroup in LDS for its 4 waves.
+//            With one K split it applies ReLU and writes H (16-bit); with
+//            several it writes fp32 partials and `up_finalize` sums them.
+//   down   - y = H W2t[S] on MFMA: a workgroup owns 64 batch rows x 256
+//            output columns over a range of the selected neurons; the
+//            gathered W2t rows are staged in LDS and read back transposed
+//            (ds_read_b64_tr_b16) as B operands, H comes from LDS as A.
+//            Split ranges of neurons write fp32 partials that
+//            `down_finalize` sums in a fixed order.
+// The selection count is read on the device, so union -> up -> down needs no
+// host synchronisation; grids are sized for the caller's upper bound n_max
+// and workgroups past the actual count exit or mask.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sha_device.h"
+#include "sha_launch.h"
+
+namespace sha {
+namespace {
+
+using namespace detail;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_vs_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) fp16x4_vs_t lds_f16x4_t;
+
+template <int DT>
+struct Mx;
+
+template <>
+struct Mx<kBF16> {
+  __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static uint2 tr_read(const lds_char_t* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p)));
+  }
+  __device__ static uint32_t pack(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2_t));
+  }
+};
+
+template <>
+struct Mx<kF16> {
+  __device__ static f32x4 mma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ static uint2 tr_read(const lds_char_t* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4_t*)(p)));
+  }
+  __device__ static uint32_t pack(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, f16x2_t));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// union of the rows' neuron lists: one flag byte per neuron in a workspace
+// ---------------------------------------------------------------------------
+constexpr int kUnionThreads = 1024;
+
+// flags[0 .. D) = 0 (16-byte stores; the flag buffer is padded to 256 bytes).
+__global__ __launch_bounds__(256) void sha_mlp_union_clear_kernel(uint8_t* flags, int D) {
+  const int n16 = (D + 15) / 16;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256)
+    reinterpret_cast<uint4*>(flags)[i] = make_uint4(0, 0, 0, 0);
+}
+
+// flags[j] = 1 for every entry j in [0, D).  Concurrent stores of the same
+// value to one byte need no atomics and leave the same result in any order.
+__global__ __launch_bounds__(256) void sha_mlp_union_mark_kernel(const int32_t* rows, int total,
+                                                                 int D, uint8_t* flags) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+    const int j = rows[i];
+    if (j >= 0 && j < D) flags[j] = 1;
+  }
+}
+
+// One workgroup: exclusive scan of the flags in ascending neuron order, each
+// set flag writes its neuron id at its rank; the total goes to *n_sel.
+__global__ __launch_bounds__(kUnionThreads) void sha_mlp_union_compact_kernel(
+    const uint8_t* flags, int D, int32_t* sel, int32_t* n_sel) {
+  __shared__ uint32_t wave_sums[kUnionThreads / 64];
+  __shared__ uint32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0u;
+  __syncthreads();
+  // each thread owns 16 consecutive flags per step
+  for (int base = 0; base < D; base += kUnionThreads * 16) {
+    const int j0 = base + tid * 16;
+    uint4 f = make_uint4(0, 0, 0, 0);
+    if (j0 < D) f = reinterpret_cast<const uint4*>(flags)[j0 / 16];
+    // flags past D in the last word are zero (cleared padding)
+    const uint32_t w[4] = {f.x, f.y, f.z, f.w};
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cnt += __popc(w[q] & 0x01010101u);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    uint32_t pos = carry;
+    for (int q = 0; q < wave; ++q) pos += wave_sums[q];
+    const uint32_t block_end = pos + incl;
+    pos += incl - cnt;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((w[q] >> (8 * e)) & 1u) sel[pos++] = j0 + 4 * q + e;
+    __syncthreads();
+    if (tid == kUnionThreads - 1) carry = block_end;
+    __syncthreads();
+  }
+  if (tid == 0) *n_sel = static_cast<int32_t>(carry);
+}
+
+// ---------------------------------------------------------------------------
+// up projection: H = relu(x W1t[S]^T)
+// ---------------------------------------------------------------------------
+constexpr int kUpKc = 256;                   // K chunk (elements)
+constexpr int kUpXPitch = kUpKc * 2 + 16;    // LDS bytes per x row (conflict-free b128 reads)
+
+__device__ __forceinline__ int sel_count(const MlpArgs& a) {
+  const int n = *a.n_sel;
+  return n < 0 ? 0 : (n > a.n_max ? a.n_max : n);
+}
+
+// Weight row of selection entry n (< count); entries outside [0, D) read row 0
+// and are zeroed where their activation is produced.
+__device__ __forceinline__ int sel_row(const MlpArgs& a, int n) {
+  const int r = a.sel[n];
+  return (r >= 0 && r < a.D) ? r : 0;
+}
+__device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
+  if (n >= count) return false;
+  const int r = a.sel[n];
+  return r >= 0 && r < a.D;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void sha_mlp_up_kernel(MlpArgs a) {
+  using M = Mx<DT>;
+  __shared__ __attribute__((aligned(16))) char xs[64 * kUpXPitch];
+  const int n_sel = sel_count(a);
+  const int nb0 = blockIdx.x * 64;
+  if (nb0 >= n_sel) return;
+  const int split = blockIdx.y;
+  const int b0 = blockIdx.z * 64;
+  const int kbeg = split * a.up_kper;
+  const int kend = min(kbeg + a.up_kper, a.d);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c = lane & 15;
+  const int n = nb0 + 16 * wave + c;
+  const int row = sel_row(a, min(n, n_sel - 1));
+  const char* wrow = static_cast<const char*>(a.w1t) + static_cast<size_t>(row) * a.d * 2;
+  lds_char_t* const xl = (lds_char_t*)(xs);
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // x pieces of a K chunk: 64 rows x 32 pieces of 16 B, 8 per thread.
+  auto load_x = [&](int k0, uint4 (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 5, piece = idx & 31;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (b0 + r < a.B)
+        v[i] = ld16(static_cast<const char*>(a.x) +
+                    (static_cast<size_t>(b0 + r) * a.d + k0 + piece * 8) * 2);
+    }
+  };
+
+  // Software pipeline: the weights and the x pieces of chunk i+1 are in
+  // flight while chunk i is multiplied.
+  uint4 wcur[8], wnext[8], xcur[8], xnext[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) wcur[kc] = ld16_stream(wrow + (kbeg + 32 * kc + 8 * q4) * 2);
+  load_x(kbeg, xcur);
+
+  for (int k0 = kbeg; k0 < kend; k0 += kUpKc) {
+    const bool more = k0 + kUpKc < kend;
+    if (more) {
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        wnext[kc] = ld16_stream(wrow + (k0 + kUpKc + 32 * kc + 8 * q4) * 2);
+      load_x(k0 + kUpKc, xnext);
+    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 5, piece = idx & 31;
+      *(lds_u32x4_t*)(xl + r * kUpXPitch + piece * 16) = __builtin_bit_cast(u32x4_t, xcur[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const uint4 xb = __builtin_bit_cast(
+            uint4, *(const lds_u32x4_t*)(xl + (nb * 16 + c) * kUpXPitch + (32 * kc + 8 * q4) * 2));
+        acc[nb] = M::mma(wcur[kc], xb, acc[nb]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        wcur[i] = wnext[i];
+        xcur[i] = xnext[i];
+      }
+    }
+  }
+
+  // lane holds H^T[n = nb0 + 16 wave + 4 q4 + r][b = b0 + 16 nb + c]
+  const int nbase = nb0 + 16 * wave + 4 * q4;
+  // Entries outside [0, D) (and past the count) produce no activation.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (!sel_valid(a, nbase + r, n_sel)) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[nb][r] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int b = b0 + 16 * nb + c;
+    if (a.up_splits == 1) {
+      const uint32_t lo = M::pack(fmaxf(acc[nb][0], 0.f), fmaxf(acc[nb][1], 0.f));
+      const uint32_t hi = M::pack(fmaxf(acc[nb][2], 0.f), fmaxf(acc[nb][3], 0.f));
+      *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
+                                (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
+    } else {
+      float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
+      *reinterpret_cast<float4*>(p) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+    }
+  }
+}
+
+// H = relu(sum of the K-split partials), fixed order; one thread per 4 neurons.
+template <int DT>
+__global__ __launch_bounds__(256) void sha_mlp_up_finalize_kernel(MlpArgs a) {
+  using M = Mx<DT>;
+  const int n_sel = sel_count(a);
+  const size_t quads = static_cast<size_t>(a.b_pad) * (a.n_pad / 4);
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < quads; i += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t b = i / (a.n_pad / 4);
+    const int n4 = static_cast<int>(i % (a.n_pad / 4)) * 4;
+    if (n4 >= n_sel) continue;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < a.up_splits; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(
+          a.up_part + (static_cast<size_t>(sp) * a.b_pad + b) * a.n_pad + n4);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const uint32_t lo = M::pack(fmaxf(s.x, 0.f), fmaxf(s.y, 0.f));
+    const uint32_t hi = M::pack(fmaxf(s.z, 0.f), fmaxf(s.w, 0.f));
+    *reinterpret_cast<uint2*>(static_cast<char*>(a.h) + (b * a.n_pad + n4) * 2) = make_uint2(lo, hi);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down projection: y = H W2t[S]
+// ---------------------------------------------------------------------------
+constexpr int kDnKc = 64;                   // neurons per LDS chunk (2 MFMA K steps)
+constexpr int kDnCols = 256;                // output columns per workgroup
+constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 B: conflict-free transposed reads
+constexpr int kDnHPitch = kDnKc * 2 + 16;   // 144 B: conflict-free H reads
+
+template <int DT>
+__global__ __launch_bounds__(256) void sha_mlp_down_kernel(MlpArgs a) {
+  using M = Mx<DT>;
+  __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
+  __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
+  const int n_sel = sel_count(a);
+  const int col0 = blockIdx.x * kDnCols;
+  const int split = blockIdx.y;
+  const int b0 = blockIdx.z * 64;
+  // This split's neuron range (whole MFMA K steps).
+  const int per = ((n_sel + a.dn_splits - 1) / a.dn_splits + 31) / 32 * 32;
+  const int nbeg = min(split * per, n_sel);
+  const int nend = min(nbeg + per, n_sel);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c = lane & 15;
+  lds_char_t* const wl = (lds_char_t*)(ws_);
+  lds_char_t* const hl = (lds_char_t*)(hs_);
+
+  f32x4 acc[4][4];  // [m block (batch)][n block (columns)]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Gathered W2t rows of a chunk: 64 rows x 512 B = 2048 pieces (8 per
+  // thread); H chunk: 64 rows x 128 B = 512 pieces (2 per thread), neurons at
+  // or past nend read as zero.
+  auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 5, piece = idx & 31;
+      const int row = sel_row(a, min(k0 + r, nend - 1));
+      wv[i] = ld16_stream(static_cast<const char*>(a.w2t) +
+                          (static_cast<size_t>(row) * a.d + col0 + piece * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 3, piece = idx & 7;
+      const int nn = k0 + piece * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      const char* src = static_cast<const char*>(a.h) + (static_cast<size_t>(b0 + r) * a.n_pad + nn) * 2;
+      if (nn + 8 <= nend) {
+        v = ld16(src);
+      } else if (nn < nend) {
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+        uint16_t t[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = (nn + e < nend) ? s16[e] : 0;
+        v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
+                       t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
+      }
+      hv[i] = v;
+    }
+  };
+
+  // Software pipeline: chunk i+1 is in flight while chunk i is multiplied.
+  uint4 wcur[8], hcur[2], wnext[8], hnext[2];
+  if (nbeg < nend) load_chunk(nbeg, wcur, hcur);
+  for (int k0 = nbeg; k0 < nend; k0 += kDnKc) {
+    const bool more = k0 + kDnKc < nend;
+    if (more) load_chunk(k0 + kDnKc, wnext, hnext);
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 5, piece = idx & 31;
+      *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, wcur[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i;
+      const int r = idx >> 3, piece = idx & 7;
+      *(lds_u32x4_t*)(hl + r * kDnHPitch + piece * 16) = __builtin_bit_cast(u32x4_t, hcur[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kDnKc / 32; ++ks) {
+      // K-slot order of a 32-neuron step: lane group q4 owns neurons
+      // 4q4 .. 4q4+3 and 16+4q4 .. 16+4q4+3 of the step.
+      uint4 ha[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const lds_char_t* hr = hl + (16 * mb + c) * kDnHPitch + ks * 64;
+        const u32x2_t p0 = *(const lds_u32x2_t*)(hr + 8 * q4);
+        const u32x2_t p1 = *(const lds_u32x2_t*)(hr + 32 + 8 * q4);
+        ha[mb] = make_uint4(p0.x, p0.y, p1.x, p1.y);
+      }
+      const int trow = ks * 32 + 4 * q4 + (c >> 2);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int cb = (64 * wave + 16 * nb) * 2 + (c & 3) * 8;
+        const uint2 x0 = M::tr_read(wl + trow * kDnWPitch + cb);
+        const uint2 x1 = M::tr_read(wl + (trow + 16) * kDnWPitch + cb);
+        const uint4 wb = make_uint4(x0.x, x0.y, x1.x, x1.y);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = M::mma(ha[mb], wb, acc[mb][nb]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wcur[i] = wnext[i];
+      hcur[0] = hnext[0];
+      hcur[1] = hnext[1];
+    }
+  }
+
+  // lane holds y[b = b0 + 16 mb + 4 q4 + r][col = col0 + 64 wave + 16 nb + c]
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = b0 + 16 * mb + 4 * q4 + r;
+      if (b >= a.B) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = col0 + 64 * wave + 16 * nb + c;
+        if (a.dn_splits == 1)
+          Elem<DT>::store(a.y, static_cast<size_t>(b) * a.d + col, acc[mb][nb][r]);
+        else
+          a.dn_part[(static_cast<size_t>(split) * a.b_pad + b) * a.d + col] = acc[mb][nb][r];
+      }
+    }
+}
+
+// y = sum of the neuron-split partials, fixed order.
+template <int DT>
+__global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
+  const size_t total = static_cast<size_t>(a.B) * a.d;
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t b = i / a.d, col = i % a.d;
+    float s = 0.f;
+    for (int sp = 0; sp < a.dn_splits; ++sp)
+      s += a.dn_part[(static_cast<size_t>(sp) * a.b_pad + b) * a.d + col];
+    Elem<DT>::store(a.y, i, s);
+  }
+}
+
+template <int DT>
+hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
+  const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
+  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(a.n_pad / 64, a.up_splits, btiles), dim3(256),
+                     0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.up_splits > 1) {
+    const size_t quads = static_cast<size_t>(a.b_pad) * (a.n_pad / 4);
+    const unsigned blocks = static_cast<unsigned>(quads < 256 * 1024 ? (quads + 255) / 256 : 1024);
+    hipLaunchKernelGGL((sha_mlp_up_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((sha_mlp_down_kernel<DT>), dim3(a.d / kDnCols, a.dn_splits, btiles),
+                     dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.dn_splits > 1) {
+    const size_t total = static_cast<size_t>(a.B) * a.d;
+    const unsigned blocks = static_cast<unsigned>(total < 256 * 1024 ? (total + 255) / 256 : 1024);
+    hipLaunchKernelGGL((sha_mlp_down_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
+                            uint8_t* flags, hipStream_t st) {
+  const int n16 = (D + 15) / 16;
+  hipLaunchKernelGGL(sha_mlp_union_clear_kernel, dim3(min((n16 + 255) / 256, 1024)), dim3(256), 0,
+                     st, flags, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (total > 0) {
+    hipLaunchKernelGGL(sha_mlp_union_mark_kernel, dim3(min((total + 255) / 256, 2048)), dim3(256),
+                       0, st, rows, total, D, flags);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(sha_mlp_union_compact_kernel, dim3(1), dim3(kUnionThreads), 0, st, flags, D,
+                     sel, n_sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_selective_mlp(const MlpArgs& a, int dtype, hipStream_t st) {
+  return dtype == kF16 ? launch_mlp_t<kF16>(a, st) : launch_mlp_t<kBF16>(a, st);
+}
+
+
+}  // namespace sha

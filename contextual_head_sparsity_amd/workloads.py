@@ -179,3 +179,58 @@ def make_workload(w: Workload, device="cpu", seed_offset: int = 0):
     idx = torch.from_numpy(sample_index(w)).to(device)
     o = sentinel_like(w, device)
     return q, k, v, idx, o
+
+
+# ---------------------------------------------------------------------------
+# Selective MLP workloads (OPT MLP shapes: d model width, D = 4 d neurons)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    """One selective-MLP layer call: batch rows each activating k_row neurons."""
+
+    name: str
+    B: int
+    d: int
+    D: int
+    k_row: int        # neurons each row's router activates
+    dtype: str        # "f16" | "bf16"
+    seed: int = 0
+
+    def with_(self, **kw) -> "MlpWorkload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def weight_bytes_per_neuron(self) -> int:
+        return 2 * self.d * 2      # one W1^T row and one W2^T row, 16-bit
+
+
+MLP_WORKLOADS = {
+    "tiny_mlp_bf16": MlpWorkload("tiny_mlp_bf16", B=3, d=256, D=1000, k_row=50, dtype="bf16", seed=11),
+    "opt6.7b_mlp_f16": MlpWorkload("opt6.7b_mlp_f16", B=16, d=4096, D=16384, k_row=1638,
+                                   dtype="f16", seed=12),
+    "opt66b_mlp_bf16": MlpWorkload("opt66b_mlp_bf16", B=64, d=9216, D=36864, k_row=3686,
+                                   dtype="bf16", seed=13),
+}
+
+
+def sample_row_neurons(w: MlpWorkload) -> np.ndarray:
+    """Each row's active neurons (a router's per-row top-k), int32 [B, k_row],
+    distinct per row, drawn uniformly without replacement from seed."""
+    rng = np.random.default_rng(3000 + w.seed)
+    return np.stack([np.sort(rng.choice(w.D, w.k_row, replace=False))
+                     for _ in range(w.B)]).astype(np.int32)
+
+
+def make_mlp(w: MlpWorkload, device="cpu"):
+    """x [B, d] ~ N(0, 1); w1t ~ N(0, 1/d) and w2t ~ N(0, 1/D), both [D, d]
+    (neuron-major), so activations and outputs are O(1); rounded once."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(4000 + w.seed)
+    dt = DTYPES[w.dtype]
+    x = _randn((w.B, w.d), gen, device).to(dt)
+    w1t = _randn((w.D, w.d), gen, device).mul_(1.0 / math.sqrt(w.d)).to(dt)
+    w2t = _randn((w.D, w.d), gen, device).mul_(1.0 / math.sqrt(w.D)).to(dt)
+    rows = torch.from_numpy(sample_row_neurons(w)).to(device)
+    return x, w1t, w2t, rows

@@ -170,6 +170,56 @@ int sha_plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
 size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
                            sha_dtype dtype, int nsplit, int num_cus);
 
+/*
+ * Selective MLP ("Selective GEMM") over the batch union of active neurons.
+ * Polar Sparsity notes (papernotes.org), 方法详解 > 关键设计 > "MLP 层动态稀疏":
+ * MLP_{S_B}(x) = sigma(x W1[:, S_B]) W2[:, S_B]^T, where S_B is the union of
+ * the active neurons of every row of the batch and the index selection is
+ * fused into the matrix products.  sigma is ReLU (the pages apply the
+ * selective MLP to OPT models); the equation has no bias and none is added.
+ *
+ * Weights are stored neuron-major: w1t = W1^T and w2t = W2^T, both [D, d]
+ * row-major, so neuron j's input and output weights are rows j.  x and y are
+ * [B, d].  f16 and bf16 only (matrix cores; SHA_ERR_UNSUPPORTED otherwise);
+ * d must be a multiple of 256 (SHA_ERR_UNSUPPORTED).  Accumulation is fp32;
+ * relu(x W1[:, S]) is rounded once to the element type before the second
+ * product.
+ */
+
+/*
+ * S_B on the device: the sorted union of the entries of row_neurons [B, k]
+ * (int32, device) that lie in [0, D) (others, e.g. -1 padding, are skipped).
+ * Writes the union to sel[0 .. n-1] (sel must hold min(D, B*k) entries) and
+ * n to *n_sel (device int32).  Deterministic; no host synchronisation.
+ *   workspace: caller-owned device buffer of at least
+ *              sha_mlp_union_workspace_bytes(D) bytes (one flag byte per
+ *              neuron, 256-byte padded), 16-byte aligned.
+ * Errors: D < 1, B < 0 or k < 0 -> SHA_ERR_INVALID_ARG; null sel / n_sel
+ * (or row_neurons when B*k > 0) -> SHA_ERR_INVALID_ARG; short workspace ->
+ * SHA_ERR_WORKSPACE.
+ */
+size_t sha_mlp_union_workspace_bytes(int D);
+sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_t* sel,
+                         int32_t* n_sel, hipStream_t stream, void* workspace,
+                         size_t workspace_bytes);
+
+/*
+ * y = relu(x w1t[S]^T) w2t[S] for S = sel[0 .. *n_sel - 1].
+ *   sel, n_sel: device int32; *n_sel is read on the device and clamped to
+ *               [0, n_max]; selection entries outside [0, D) contribute
+ *               nothing.  n_max (host, 0 <= n_max <= D) bounds the count and
+ *               sizes the grids and the workspace.
+ *   workspace : caller-owned device buffer of at least
+ *               sha_selective_mlp_workspace_bytes(B, d, D, n_max, num_cus = 0)
+ *               bytes, 16-byte aligned; contents on entry do not matter.
+ * B == 0 is an empty call.  y is fully written (zeros when S is empty).
+ */
+size_t sha_selective_mlp_workspace_bytes(int B, int d, int D, int n_max, int num_cus);
+sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, const int32_t* sel,
+                             const int32_t* n_sel, int n_max, int B, int d, int D, void* y,
+                             hipStream_t stream, sha_dtype dtype, void* workspace,
+                             size_t workspace_bytes);
+
 /* Human-readable name of a status code (static storage). */
 const char* sha_status_string(sha_status s);
 /* Raw hipError_t of the last SHA_ERR_HIP returned on the calling thread. */

@@ -20,8 +20,9 @@ Readings where the pages are silent:
   * Storage is neuron-major: w1t = W1^T and w2t = W2^T, both [D, d], so that
     neuron j's input weights and output weights are each one contiguous row.
     In this notation y = relu(x w1t[S]^T) w2t[S].
-  * A row's neuron list may hold -1 (or any entry outside [0, D)) as padding;
-    such entries are skipped.  The union is returned sorted ascending.
+  * A row's neuron list, and the selection itself, may hold -1 (or any entry
+    outside [0, D)) as padding; such entries are skipped.  The union is
+    returned sorted ascending.
 """
 from __future__ import annotations
 
@@ -62,8 +63,7 @@ def selective_mlp_ref(x, w1t, w2t, sel) -> np.ndarray:
     if X.ndim != 2 or W1t.ndim != 2 or W2t.shape != W1t.shape or W1t.shape[1] != X.shape[1]:
         raise ValueError("x [B, d], w1t / w2t [D, d] required")
     D = W1t.shape[0]
-    if S.size and (S.min() < 0 or S.max() >= D):
-        raise ValueError("selected neuron outside [0, D)")
+    S = S[(S >= 0) & (S < D)]               # padding entries select nothing
     if S.size == 0:
         return np.zeros((X.shape[0], X.shape[1]))
     H = np.maximum(X @ W1t[S].T, 0.0)      # [B, n]: sigma(x W1[:, S])

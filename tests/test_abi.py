@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -126,3 +126,45 @@ def test_binding_rejects_cpu_tensors():
     k = torch.zeros(1, 2, 8, 64)
     with pytest.raises(ValueError):
         bd.sha_decode(q, k, k, torch.zeros(1, 1, dtype=torch.int32))
+
+
+def test_mlp_host_validation():
+    L = bd.lib()
+    P = A16
+    # union: bad sizes, null outputs, workspace
+    big = 1 << 20
+    assert L.sha_mlp_union(P, 2, 3, 0, P, P, None, P, big) == 1
+    assert L.sha_mlp_union(P, -1, 3, 10, P, P, None, P, big) == 1
+    assert L.sha_mlp_union(P, 2, 3, 10, None, P, None, P, big) == 1
+    assert L.sha_mlp_union(None, 2, 3, 10, P, P, None, P, big) == 1
+    assert L.sha_mlp_union(P + 2, 2, 3, 10, P, P, None, P, big) == 3
+    assert L.sha_mlp_union_workspace_bytes(1000) == 1024
+    assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, P, 1023) == 4
+    assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, None, big) == 4
+
+    def mlp(x=P, w1=P, w2=P, sel=P, n=P, n_max=64, B=4, d=256, D=1000, y=P, dtype=2, ws=P,
+            wsb=1 << 30):
+        return L.sha_selective_mlp(x, w1, w2, sel, n, n_max, B, d, D, y, None, dtype, ws, wsb)
+
+    assert mlp(d=200) == 2            # d must be a multiple of 256
+    assert mlp(dtype=0) == 2          # f32 has no matrix-core path here
+    assert mlp(n_max=1001) == 1       # n_max > D
+    assert mlp(B=-1) == 1
+    assert mlp(B=0, x=None, w1=None, w2=None, sel=None, n=None, y=None) == 0   # empty call
+    assert mlp(sel=None) == 1
+    assert mlp(x=P + 8) == 3
+    assert mlp(ws=None) == 4
+    need = L.sha_selective_mlp_workspace_bytes(4, 256, 1000, 64, 256)
+    assert need > 0 and mlp(wsb=need - 1) == 4
+
+
+def test_mlp_workspace_accounting():
+    L = bd.lib()
+    # OPT-66B MLP, all 36864 neurons selected, 64 rows, 256 CUs: H (64 x 36864
+    # 16-bit) plus the down projection's fp32 partials over 8 neuron splits.
+    ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 36864, 256)
+    assert ws == 64 * 36864 * 2 + 8 * 64 * 9216 * 4
+    # a small selection splits the up projection's K as well
+    ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
+    up_splits = 9216 // 256          # one WG per split chunk, capped by the d chunks
+    assert ws == 64 * 64 * 2 + up_splits * 64 * 64 * 4   # a single down split (64 neurons)
