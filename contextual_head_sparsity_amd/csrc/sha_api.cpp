@@ -252,30 +252,41 @@ struct MlpPlan {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Grid sizes from the selection bound: the up projection has one workgroup
-// per 64 selected neurons x 64 batch rows and splits its K (d) when that is
-// fewer than two workgroups per CU; the down projection has one workgroup
-// per 256 output columns x 64 rows and splits the neuron range until it has
-// about one workgroup per CU (each split range keeps >= 64 neurons).
+// Grid sizes from the selection bound.  Both products stream weights, so the
+// planner fills the chip without leaving a small second round of work.
+// Residency from the kernels' register use on gfx950: the up projection's
+// waves (224 registers) fit 2 per SIMD, 8 per CU.
+//   up  : one wave per 64 selected neurons x 64 batch rows; its K (d) is
+//         split so that the waves fill the 8-per-CU slots once (at most 16
+//         splits).
+//   down: one workgroup per 256 output columns x 64 rows; the neuron range is
+//         split for about two workgroups per CU (each range keeps >= 64
+//         neurons, at most 64 splits).
+// The constants come from a split sweep of the OPT-66B MLP on MI355X.
+constexpr int kUpWavesPerCu = 8;
+constexpr int kDownWgsPerCu = 2;
+
 MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   MlpPlan p{};
   const int cus = device_cus(num_cus);
   p.n_pad = ((n_max > 0 ? n_max : 1) + 63) / 64 * 64;
   p.b_pad = (B + 63) / 64 * 64;
-  const long long up_wgs = static_cast<long long>(p.n_pad / 64) * (p.b_pad / 64);
-  long long us = (2LL * cus + up_wgs - 1) / up_wgs;
-  const int kchunks = d / 256;
+  const long long up_items = static_cast<long long>(p.n_pad / 64) * (p.b_pad / 64);
+  long long us = static_cast<long long>(kUpWavesPerCu) * cus / up_items;
+  const int kchunks = d / 128;
   if (us > kchunks) us = kchunks;
-  if (us > 64) us = 64;
+  if (us > 16) us = 16;
   if (us < 1) us = 1;
-  p.up_kper = (kchunks + static_cast<int>(us) - 1) / static_cast<int>(us) * 256;
+  if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
+  p.up_kper = (kchunks + static_cast<int>(us) - 1) / static_cast<int>(us) * 128;
   p.up_splits = (d + p.up_kper - 1) / p.up_kper;
-  const long long dn_wgs = static_cast<long long>(d / 256) * (p.b_pad / 64);
-  long long ds = (static_cast<long long>(cus) + dn_wgs - 1) / dn_wgs;
+  const long long dn_items = static_cast<long long>(d / 256) * (p.b_pad / 64);
+  long long ds = static_cast<long long>(kDownWgsPerCu) * cus / dn_items;
   const long long ds_max = n_max / 64 > 1 ? n_max / 64 : 1;
   if (ds > ds_max) ds = ds_max;
   if (ds > 64) ds = 64;
   if (ds < 1) ds = 1;
+  if (env_int("SHA_MLP_DN_SPLITS", 0) > 0) ds = env_int("SHA_MLP_DN_SPLITS", 0);  // tuning hook
   p.dn_splits = static_cast<int>(ds);
   p.h_bytes = round256(static_cast<size_t>(p.b_pad) * p.n_pad * 2);
   p.up_bytes = p.up_splits > 1 ? round256(static_cast<size_t>(p.up_splits) * p.b_pad * p.n_pad * 4) : 0;

@@ -14,12 +14,12 @@
 //            then one workgroup scans the flags and writes the marked neurons
 //            in ascending order and their count, on device (deterministic).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
-//            a workgroup owns 64 selected neurons x 64 batch rows; the
-//            selected weight rows stream from HBM straight into A operands
-//            (non-temporal 128-bit loads, one K chunk prefetched ahead), the
-//            x chunk is staged once per workgroup in LDS for its 4 waves.
-//            With one K split it applies ReLU and writes H (16-bit); with
-//            several it writes fp32 partials and `up_finalize` sums them.
+//            each wave owns 64 selected neurons x 64 batch rows over a K
+//            range and streams the selected weight rows straight into A
+//            operands (non-temporal 128-bit loads, 8 KiB per batch) with x
+//            pieces from L2 as B operands; no LDS, no barriers.  With one K
+//            split it applies ReLU and writes H (16-bit); with several it
+//            writes fp32 partials and `up_finalize` sums them.
 //   down   - y = H W2t[S] on MFMA: a workgroup owns 64 batch rows x 256
 //            output columns over a range of the selected neurons; the
 //            gathered W2t rows are staged in LDS and read back transposed
@@ -156,8 +156,7 @@ __global__ __launch_bounds__(kUnionThreads) void sha_mlp_union_compact_kernel(
 // ---------------------------------------------------------------------------
 // up projection: H = relu(x W1t[S]^T)
 // ---------------------------------------------------------------------------
-constexpr int kUpKc = 256;                   // K chunk (elements)
-constexpr int kUpXPitch = kUpKc * 2 + 16;    // LDS bytes per x row (conflict-free b128 reads)
+constexpr int kUpSteps = 2;   // MFMA K steps (of 32) per iteration: 8 KiB of weights in flight
 
 __device__ __forceinline__ int sel_count(const MlpArgs& a) {
   const int n = *a.n_sel;
@@ -176,104 +175,93 @@ __device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
   return r >= 0 && r < a.D;
 }
 
+// One wave owns 64 selected neurons (4 MFMA row blocks) x 64 batch rows
+// (4 column blocks) over a K range; waves are independent (no LDS, no
+// barriers), so a CU keeps several waves' 8 KiB weight batches in flight.
+// The x pieces (B operands) are re-read from L2 by every wave of the same K
+// range: as many bytes as the wave's weights.
+// Wave id = ((btile * up_splits) + split) * nblocks + nblock.
 template <int DT>
 __global__ __launch_bounds__(256) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
-  __shared__ __attribute__((aligned(16))) char xs[64 * kUpXPitch];
+  const int nblocks = a.n_pad / 64;
+  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nblk = t % nblocks;
+  t /= nblocks;
+  const int split = t % a.up_splits;
+  const int btile = t / a.up_splits;
+  if (btile >= a.b_pad / 64) return;          // padding waves of the last workgroup
   const int n_sel = sel_count(a);
-  const int nb0 = blockIdx.x * 64;
-  if (nb0 >= n_sel) return;
-  const int split = blockIdx.y;
-  const int b0 = blockIdx.z * 64;
+  const int n0 = nblk * 64;
+  if (n0 >= n_sel) return;
+  const int b0 = btile * 64;
   const int kbeg = split * a.up_kper;
   const int kend = min(kbeg + a.up_kper, a.d);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4, c = lane & 15;
-  const int n = nb0 + 16 * wave + c;
-  const int row = sel_row(a, min(n, n_sel - 1));
-  const char* wrow = static_cast<const char*>(a.w1t) + static_cast<size_t>(row) * a.d * 2;
-  lds_char_t* const xl = (lds_char_t*)(xs);
-
-  f32x4 acc[4];
+  const char* wrow[4];
+  const char* xrow[4];
+  bool xok[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // x pieces of a K chunk: 64 rows x 32 pieces of 16 B, 8 per thread.
-  auto load_x = [&](int k0, uint4 (&v)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 5, piece = idx & 31;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (b0 + r < a.B)
-        v[i] = ld16(static_cast<const char*>(a.x) +
-                    (static_cast<size_t>(b0 + r) * a.d + k0 + piece * 8) * 2);
-    }
-  };
-
-  // Software pipeline: the weights and the x pieces of chunk i+1 are in
-  // flight while chunk i is multiplied.
-  uint4 wcur[8], wnext[8], xcur[8], xnext[8];
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) wcur[kc] = ld16_stream(wrow + (kbeg + 32 * kc + 8 * q4) * 2);
-  load_x(kbeg, xcur);
-
-  for (int k0 = kbeg; k0 < kend; k0 += kUpKc) {
-    const bool more = k0 + kUpKc < kend;
-    if (more) {
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        wnext[kc] = ld16_stream(wrow + (k0 + kUpKc + 32 * kc + 8 * q4) * 2);
-      load_x(k0 + kUpKc, xnext);
-    }
-    __syncthreads();  // the previous chunk's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 5, piece = idx & 31;
-      *(lds_u32x4_t*)(xl + r * kUpXPitch + piece * 16) = __builtin_bit_cast(u32x4_t, xcur[i]);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint4 xb = __builtin_bit_cast(
-            uint4, *(const lds_u32x4_t*)(xl + (nb * 16 + c) * kUpXPitch + (32 * kc + 8 * q4) * 2));
-        acc[nb] = M::mma(wcur[kc], xb, acc[nb]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        wcur[i] = wnext[i];
-        xcur[i] = xnext[i];
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int row = sel_row(a, min(n0 + 16 * i + c, n_sel - 1));
+    wrow[i] = static_cast<const char*>(a.w1t) + (static_cast<size_t>(row) * a.d + 8 * q4) * 2;
+    const int b = b0 + 16 * i + c;
+    xok[i] = b < a.B;
+    xrow[i] = static_cast<const char*>(a.x) + (static_cast<size_t>(xok[i] ? b : 0) * a.d + 8 * q4) * 2;
   }
 
-  // lane holds H^T[n = nb0 + 16 wave + 4 q4 + r][b = b0 + 16 nb + c]
-  const int nbase = nb0 + 16 * wave + 4 * q4;
-  // Entries outside [0, D) (and past the count) produce no activation.
+  f32x4 acc[4][4];  // [neuron block][batch block]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (!sel_valid(a, nbase + r, n_sel)) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[nb][r] = 0.f;
-    }
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = kbeg; k < kend; k += 32 * kUpSteps) {
+    uint4 wv[kUpSteps][4], xv[kUpSteps][4];
+#pragma unroll
+    for (int u = 0; u < kUpSteps; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[u][i] = ld16_stream(wrow[i] + (k + 32 * u) * 2);
+#pragma unroll
+    for (int u = 0; u < kUpSteps; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xv[u][i] = xok[i] ? ld16(xrow[i] + (k + 32 * u) * 2) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kUpSteps; ++u)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = M::mma(wv[u][mb], xv[u][nb], acc[mb][nb]);
   }
+
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b = b0 + 16 nb + c]
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int b = b0 + 16 * nb + c;
-    if (a.up_splits == 1) {
-      const uint32_t lo = M::pack(fmaxf(acc[nb][0], 0.f), fmaxf(acc[nb][1], 0.f));
-      const uint32_t hi = M::pack(fmaxf(acc[nb][2], 0.f), fmaxf(acc[nb][3], 0.f));
-      *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
-                                (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
-    } else {
-      float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
-      *reinterpret_cast<float4*>(p) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+  for (int mb = 0; mb < 4; ++mb) {
+    const int nbase = n0 + 16 * mb + 4 * q4;
+    // Entries outside [0, D) (and past the count) produce no activation.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (!sel_valid(a, nbase + r, n_sel)) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb][r] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int b = b0 + 16 * nb + c;
+      if (a.up_splits == 1) {
+        const uint32_t lo = M::pack(fmaxf(acc[mb][nb][0], 0.f), fmaxf(acc[mb][nb][1], 0.f));
+        const uint32_t hi = M::pack(fmaxf(acc[mb][nb][2], 0.f), fmaxf(acc[mb][nb][3], 0.f));
+        *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
+                                  (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
+      } else {
+        float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
+        *reinterpret_cast<float4*>(p) =
+            make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
+      }
     }
   }
 }
@@ -451,8 +439,9 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
 template <int DT>
 hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
-  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(a.n_pad / 64, a.up_splits, btiles), dim3(256),
-                     0, st, a);
+  const long long up_waves = static_cast<long long>(a.n_pad / 64) * a.up_splits * btiles;
+  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(static_cast<unsigned>((up_waves + 3) / 4)),
+                     dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.up_splits > 1) {

@@ -161,10 +161,12 @@ def test_mlp_host_validation():
 def test_mlp_workspace_accounting():
     L = bd.lib()
     # OPT-66B MLP, all 36864 neurons selected, 64 rows, 256 CUs: H (64 x 36864
-    # 16-bit) plus the down projection's fp32 partials over 8 neuron splits.
+    # 16-bit), the up projection's fp32 partials over 3 K splits (576 waves x 3
+    # fill 8 waves per CU once) and the down projection's over 14 neuron
+    # splits (36 column blocks x 14 ~ 2 workgroups per CU).
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 36864, 256)
-    assert ws == 64 * 36864 * 2 + 8 * 64 * 9216 * 4
-    # a small selection splits the up projection's K as well
+    assert ws == 64 * 36864 * 2 + 3 * 64 * 36864 * 4 + 14 * 64 * 9216 * 4
+    # a 64-neuron selection splits the up projection's K 15 ways (16 wanted,
+    # 640-element ranges) and keeps a single down split
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
-    up_splits = 9216 // 256          # one WG per split chunk, capped by the d chunks
-    assert ws == 64 * 64 * 2 + up_splits * 64 * 64 * 4   # a single down split (64 neurons)
+    assert ws == 64 * 64 * 2 + 15 * 64 * 64 * 4
