@@ -41,6 +41,7 @@ SIGNATURES = {
     "sha_mlp_union": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _S]),
     "sha_selective_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "sha_selective_mlp": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _S]),
+    "sha_router_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I]),
     "sha_status_string": (ctypes.c_char_p, [_I]),
     "sha_last_hip_error": (_I, []),
     "sha_version": (ctypes.c_char_p, []),
@@ -234,3 +235,39 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
                                  stream.cuda_stream, _DT[x.dtype], workspace.data_ptr(), need)
     _check(st, "sha_selective_mlp")
     return out
+
+
+# ---------------------------------------------------------------------------
+# attention router
+# ---------------------------------------------------------------------------
+
+def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
+    """Attention router on the device: scores = x w^T (+ bias), the top_k heads
+    per row in ascending order.  x [B, d], w [H, d] (f32 / f16 / bf16), bias
+    [H] fp32.  Returns (index [B, top_k] int32, scores [B, H] fp32)."""
+    for name, t in (("x", x), ("w", w)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D device tensor")
+    if x.dtype not in _DT or w.dtype != x.dtype:
+        raise ValueError("x and w must share float32 / float16 / bfloat16")
+    B, d = x.shape
+    H = w.shape[0]
+    if w.shape[1] != d:
+        raise ValueError("w must be [H, d]")
+    if bias is not None:
+        if not bias.is_cuda or bias.dtype != torch.float32 or bias.numel() != H:
+            raise ValueError("bias must be a float32 device tensor of H entries")
+        bias = bias.contiguous()
+    if index is None:
+        index = torch.empty((B, top_k), dtype=torch.int32, device=x.device)
+    if scores is None:
+        scores = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = lib().sha_router_topk(x.data_ptr(), w.data_ptr(),
+                                   bias.data_ptr() if bias is not None else None, B, d, H, top_k,
+                                   index.data_ptr(), scores.data_ptr(), stream.cuda_stream,
+                                   _DT[x.dtype])
+    _check(st, "sha_router_topk")
+    return index, scores

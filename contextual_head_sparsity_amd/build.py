@@ -43,7 +43,7 @@ def build(verbose: bool = True) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
-    for src in ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_mlp.hip"):
+    for src in ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_mlp.hip", "sha_router.hip"):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
               os.path.join(CSRC, src), "-o", obj])

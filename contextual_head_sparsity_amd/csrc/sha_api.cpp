@@ -483,6 +483,28 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   return SHA_OK;
 }
 
+sha_status sha_router_topk(const void* x, const void* w, const float* bias, int B, int d, int H,
+                           int top_k, int32_t* batch_head_index, float* scores,
+                           hipStream_t stream, sha_dtype dtype) {
+  if (B < 0 || d < 1 || H < 1 || top_k < 0 || top_k > H) return SHA_ERR_INVALID_ARG;
+  if (dtype != SHA_F32 && dtype != SHA_F16 && dtype != SHA_BF16) return SHA_ERR_UNSUPPORTED;
+  if (H > sha::kRouterMaxH) return SHA_ERR_UNSUPPORTED;
+  if (d % (dtype == SHA_F32 ? 4 : 8) != 0) return SHA_ERR_UNSUPPORTED;
+  if (B == 0) return SHA_OK;
+  if (!x || !w || !scores || (top_k > 0 && !batch_head_index)) return SHA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scores, 4) ||
+      (bias && !aligned(bias, 4)) || (batch_head_index && !aligned(batch_head_index, 4)))
+    return SHA_ERR_MISALIGNED;
+  sha::RouterArgs a{x, w, bias, scores, batch_head_index, B, d, H, top_k};
+  (void)hipGetLastError();
+  const hipError_t e = sha::launch_router(a, dtype, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = e;
+    return SHA_ERR_HIP;
+  }
+  return SHA_OK;
+}
+
 const char* sha_status_string(sha_status s) {
   switch (s) {
     case SHA_OK: return "SHA_OK";

@@ -70,4 +70,17 @@ hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel,
                             uint8_t* flags, hipStream_t stream);
 hipError_t launch_selective_mlp(const MlpArgs& a, int dtype, hipStream_t stream);
 
+// Attention router: scores = x w^T (+ bias), per-row top-k heads.
+constexpr int kRouterMaxH = 1024;
+struct RouterArgs {
+  const void* x;        // [B, d]
+  const void* w;        // [H, d]
+  const float* bias;    // [H] or null
+  float* scores;        // [B, H] fp32 (output)
+  int32_t* index;       // [B, top_k] (output, ascending head ids)
+  int B, d, H, top_k;
+};
+
+hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace sha

@@ -171,6 +171,28 @@ size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, in
                            sha_dtype dtype, int nsplit, int num_cus);
 
 /*
+ * Attention router: the per-request active heads (or GQA groups) that feed
+ * sha_decode / sha_decode_gqa.  Polar Sparsity notes (papernotes.org),
+ * 损失函数 / 训练策略 (the attention router is a single fully connected layer
+ * trained on the top-k of the per-head attention output norm); atlas.scime.ai
+ * summary, "Approach" (routers pick the top-k heads or GQA groups per
+ * request).
+ *     scores[b, h] = x[b, :] . w[h, :] (+ bias[h])        (fp32 accumulation)
+ *     batch_head_index[b, :] = the top_k heads of scores[b, :], ascending
+ * Ties go to the lower head id; a NaN score ranks like -inf.
+ *   x     : [B, d] device, element type dtype;  w: [H, d] device (one row per
+ *           head or group), same type;  bias: [H] fp32 device or null.
+ *   scores: [B, H] fp32 device output (always written);
+ *   batch_head_index: [B, top_k] int32 device output (may be null if top_k = 0).
+ * Limits: 1 <= H <= 1024, 0 <= top_k <= H, d a multiple of 8 (4 for f32),
+ * else SHA_ERR_INVALID_ARG / SHA_ERR_UNSUPPORTED.  B == 0 is an empty call.
+ * x and w 16-byte aligned, the others 4-byte aligned (SHA_ERR_MISALIGNED).
+ */
+sha_status sha_router_topk(const void* x, const void* w, const float* bias, int B, int d, int H,
+                           int top_k, int32_t* batch_head_index, float* scores,
+                           hipStream_t stream, sha_dtype dtype);
+
+/*
  * Selective MLP ("Selective GEMM") over the batch union of active neurons.
  * Polar Sparsity notes (papernotes.org), 方法详解 > 关键设计 > "MLP 层动态稀疏":
  * MLP_{S_B}(x) = sigma(x W1[:, S_B]) W2[:, S_B]^T, where S_B is the union of

@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -170,3 +170,17 @@ def test_mlp_workspace_accounting():
     # 640-element ranges) and keeps a single down split
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
     assert ws == 64 * 64 * 2 + 15 * 64 * 64 * 4
+
+
+def test_router_host_validation():
+    L = bd.lib()
+    P = A16
+
+    def r(x=P, w=P, bias=None, B=4, d=256, H=72, k=22, idx=P, sc=P, dtype=1):
+        return L.sha_router_topk(x, w, bias, B, d, H, k, idx, sc, None, dtype)
+
+    assert r(k=73) == 1 and r(k=-1) == 1 and r(H=0) == 1 and r(d=0) == 1
+    assert r(H=1025) == 2 and r(d=252) == 2 and r(dtype=5) == 2
+    assert r(B=0, x=None, w=None, idx=None, sc=None) == 0
+    assert r(sc=None) == 1 and r(idx=None) == 1
+    assert r(x=P + 8) == 3 and r(idx=P + 2) == 3 and r(bias=P + 2) == 3
