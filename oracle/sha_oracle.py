@@ -37,6 +37,9 @@ Readings where the pages are silent (each also checked by the tests):
     head h // G.
   * duplicate entries in a row compute the same head twice (same value).
   * Nkv must be >= 1 (an empty key set has no softmax).
+  * Per-row cache lengths (optional seqlens[B]): row b attends to its first
+    min(seqlens[b], Nkv) keys; a row whose length is <= 0 has no keys and its
+    active heads get an all-zero output (the empty weighted sum).
 """
 from __future__ import annotations
 
@@ -105,7 +108,24 @@ def _prefill(o_in, shape):
     return o
 
 
-def sha_decode_ref(q, k, v, batch_head_index, scale, o_in=None):
+def _row_lengths(seqlens, B, Nkv):
+    if seqlens is None:
+        return [Nkv] * B
+    L = np.asarray(seqlens.cpu() if torch is not None and isinstance(seqlens, torch.Tensor)
+                   else seqlens).reshape(-1)
+    if L.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    return [int(min(max(int(x), 0), Nkv)) for x in L]
+
+
+def _attend_prefix(q, K, V, s, n):
+    """attend_one over the first n keys; n == 0 gives zeros."""
+    if n == 0:
+        return np.zeros(V.shape[1])
+    return attend_one(q, K[:n], V[:n], s)
+
+
+def sha_decode_ref(q, k, v, batch_head_index, scale, o_in=None, seqlens=None):
     """Head-indexed SHA decode in fp64.
 
     Returns (O, written): O is [B, H, 1, d] float64 holding o_in (widened;
@@ -118,6 +138,7 @@ def sha_decode_ref(q, k, v, batch_head_index, scale, o_in=None):
     B, H, H_kv, Nkv, d, top_k = _check_shapes(Q, K, V, idx, gqa=False)
     G = H // H_kv
     s = _scale64(scale)
+    lens = _row_lengths(seqlens, B, Nkv)
     O = _prefill(o_in, Q.shape)
     written = np.zeros((B, H), dtype=bool)
     for b in range(B):
@@ -126,12 +147,12 @@ def sha_decode_ref(q, k, v, batch_head_index, scale, o_in=None):
             if h < 0 or h >= H:
                 continue
             g = h // G
-            O[b, h, 0, :] = attend_one(Q[b, h, 0, :], K[b, g], V[b, g], s)
+            O[b, h, 0, :] = _attend_prefix(Q[b, h, 0, :], K[b, g], V[b, g], s, lens[b])
             written[b, h] = True
     return O, written
 
 
-def sha_decode_gqa_ref(q, k, v, batch_group_index, scale, o_in=None):
+def sha_decode_gqa_ref(q, k, v, batch_group_index, scale, o_in=None, seqlens=None):
     """Group-indexed (GQA group sparsity) SHA decode in fp64.
 
     batch_group_index[b, :] lists active KV groups; every query head
@@ -144,6 +165,7 @@ def sha_decode_gqa_ref(q, k, v, batch_group_index, scale, o_in=None):
     B, H, H_kv, Nkv, d, top_k = _check_shapes(Q, K, V, gidx, gqa=True)
     G = H // H_kv
     s = _scale64(scale)
+    lens = _row_lengths(seqlens, B, Nkv)
     O = _prefill(o_in, Q.shape)
     written = np.zeros((B, H), dtype=bool)
     for b in range(B):
@@ -153,7 +175,7 @@ def sha_decode_gqa_ref(q, k, v, batch_group_index, scale, o_in=None):
                 continue
             for j in range(G):
                 h = g * G + j
-                O[b, h, 0, :] = attend_one(Q[b, h, 0, :], K[b, g], V[b, g], s)
+                O[b, h, 0, :] = _attend_prefix(Q[b, h, 0, :], K[b, g], V[b, g], s, lens[b])
                 written[b, h] = True
     return O, written
 

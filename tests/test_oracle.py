@@ -231,7 +231,35 @@ def pin_golden_closed_forms(impl):
             assert not w[b, h] and np.all(O[b, h] == 123.0), (case["name"], key)
 
 
-PINS = [pin_dense_equals_sdpa, pin_single_key_returns_v, pin_uniform_scores_give_mean,
+def pin_seqlens(impl):
+    """Per-row cache lengths: the same as slicing each row's K/V to its
+    length; full length is the default; length 1 gives V[0]; <= 0 gives zeros."""
+    rng = np.random.default_rng(23)
+    q, k, v = _rand(rng, 4, 4, 2, 20, 6)
+    idx = np.array([[0, 3], [1, 2], [3, 0], [2, 1]], dtype=np.int32)
+    lens = np.array([20, 7, 1, 0])
+    O, w = impl.mha(q, k, v, idx, 0.4, seqlens=lens)
+    O_full, _ = impl.mha(q, k, v, idx, 0.4)
+    assert np.array_equal(O[0], O_full[0], equal_nan=True)
+    for b, n in ((1, 7),):
+        Ob, _ = impl.mha(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], idx[b:b + 1], 0.4)
+        np.testing.assert_allclose(O[b], Ob[0], rtol=0, atol=1e-14)
+    for h in idx[2]:
+        assert np.array_equal(O[2, h, 0], v[2, h // 2, 0])
+    for h in idx[3]:
+        assert np.array_equal(O[3, h, 0], np.zeros(6))
+    # lengths are clamped to [0, Nkv]
+    Oc, _ = impl.mha(q, k, v, idx, 0.4, seqlens=np.array([99, 7, 1, -5]))
+    assert np.array_equal(Oc, O, equal_nan=True)
+    # group form: lengths apply to every head of the group
+    gidx = np.array([[1], [0], [1], [0]], dtype=np.int32)
+    Og, wg = impl.gqa(q, k, v, gidx, 0.4, seqlens=np.array([20, 7, 1, 0]))
+    Om, _ = impl.mha(q, k, v, np.array([[2, 3], [0, 1], [2, 3], [0, 1]], dtype=np.int32), 0.4,
+                     seqlens=np.array([20, 7, 1, 0]))
+    np.testing.assert_allclose(Og[wg], Om[wg], rtol=0, atol=1e-14)
+
+
+PINS = [pin_seqlens, pin_dense_equals_sdpa, pin_single_key_returns_v, pin_uniform_scores_give_mean,
         pin_brute_force, pin_head_order_invariant, pin_key_permutation_invariant,
         pin_key_shift_invariant, pin_value_affine, pin_sparse_subset_of_dense,
         pin_gqa_equals_repeated_mha, pin_large_scores_stable, pin_untouched_and_padding,
@@ -331,7 +359,7 @@ def _mutant_attend(kind):
 
 
 def _mutant_mha(kind):
-    def mha(q, k, v, idx, scale, o_in=None):
+    def mha(q, k, v, idx, scale, o_in=None, seqlens=None):
         Q, K, V = so.to_f64(q), so.to_f64(k), so.to_f64(v)
         idx = np.asarray(idx)
         B, H = Q.shape[:2]
@@ -349,14 +377,15 @@ def _mutant_mha(kind):
                     continue
                 h = h % H
                 g = h % H_kv if kind == "gqa_modulo" else h // G
-                O[b, h, 0] = so.attend_one(Q[b, h, 0], K[b, g], V[b, g], s)
+                n = K.shape[2] if seqlens is None else max(0, min(int(seqlens[b]), K.shape[2]))
+                O[b, h, 0] = so.attend_one(Q[b, h, 0], K[b, g, :n], V[b, g, :n], s) if n else 0.0
                 w[b, h] = True
         return O, w
     return mha
 
 
 def _mutant_gqa(kind):
-    def gqa(q, k, v, gidx, scale, o_in=None):
+    def gqa(q, k, v, gidx, scale, o_in=None, seqlens=None):
         Q, K, V = so.to_f64(q), so.to_f64(k), so.to_f64(v)
         gidx = np.asarray(gidx)
         B, H = Q.shape[:2]
@@ -373,8 +402,9 @@ def _mutant_gqa(kind):
                 heads = [g] if kind == "gqa_first_head_only" else (
                     [g + j * H_kv for j in range(G)] if kind == "gqa_strided_heads"
                     else [g * G + j for j in range(G)])
+                n = K.shape[2] if seqlens is None else max(0, min(int(seqlens[b]), K.shape[2]))
                 for h in heads:
-                    O[b, h, 0] = so.attend_one(Q[b, h, 0], K[b, g], V[b, g], s)
+                    O[b, h, 0] = so.attend_one(Q[b, h, 0], K[b, g, :n], V[b, g, :n], s) if n else 0.0
                     w[b, h] = True
         return O, w
     return gqa
