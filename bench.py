@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=wl.HEADLINE, choices=list(wl.WORKLOADS))
     p.add_argument("--nsplit", type=int, default=0, help="0 = library plan")
+    p.add_argument("--kv-layout", default="contig",
+                   help="contig | bnhd ([B, Nkv, H_kv, d] cache) | pagedP (pool of P-row pages)")
     p.add_argument("--copies", type=int, default=0,
                    help="rotating K/V copies (0 = enough that consecutive steps share no bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -268,6 +270,27 @@ def bench_mlp(args):
     print(json.dumps(out), flush=True)
 
 
+def to_pages(w, ks, vs, page, dev):
+    """Move each K/V copy into a pool of `page`-row pages [num_pages, page, H_kv, d]
+    placed in a seeded random page order; returns [num_pages, H_kv, page, d]
+    views and the block table."""
+    if w.Nkv % page:
+        raise SystemExit(f"Nkv={w.Nkv} is not a multiple of the page size {page}")
+    npg = w.Nkv // page
+    perm = np.random.default_rng(w.seed).permutation(w.B * npg).astype(np.int32)
+    bt = torch.from_numpy(perm).view(w.B, npg).to(dev)
+    order = bt.view(-1).long()
+
+    def pool(t):
+        src = t.view(w.B, w.H_kv, npg, page, w.d).permute(0, 2, 3, 1, 4).reshape(-1, page, w.H_kv,
+                                                                                   w.d)
+        p = torch.empty_like(src)
+        p[order] = src
+        return p.permute(0, 2, 1, 3)
+
+    return [pool(t) for t in ks], [pool(t) for t in vs], bt
+
+
 def main():
     args = parse()
     if args.mlp:
@@ -301,13 +324,32 @@ def main():
         vs.append(vc)
     nsplit = args.nsplit or sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa,
                                             q.dtype)
-    ws_bytes = sha.workspace_bytes(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa, q.dtype, nsplit)
+    layout = args.kv_layout
+    page = int(layout[5:]) if layout.startswith("paged") else 0
+    if page:
+        ws_bytes = sha.workspace_bytes_paged(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa, q.dtype,
+                                             nsplit, page)
+    else:
+        ws_bytes = sha.workspace_bytes(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa, q.dtype,
+                                       nsplit)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    bt = None
+    if layout == "bnhd":
+        ks = [t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in ks]
+        vs = [t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in vs]
+    elif page:
+        ks, vs, bt = to_pages(w, ks, vs, page, dev)
+    elif layout != "contig":
+        raise SystemExit(f"unknown --kv-layout {layout}")
 
     def call(i, index=idx):
-        fn(q, ks[i % copies], vs[i % copies], index, scale=w.scale, out=o, nsplit=nsplit,
-           workspace=ws, stream=stream)
+        if page:
+            sha.sha_decode_paged(q, ks[i % copies], vs[i % copies], bt, index, w.Nkv, gqa=w.gqa,
+                                 scale=w.scale, out=o, nsplit=nsplit, workspace=ws, stream=stream)
+        else:
+            fn(q, ks[i % copies], vs[i % copies], index, scale=w.scale, out=o, nsplit=nsplit,
+               workspace=ws, stream=stream)
 
     ms, ev = time_calls(call, args.steps, args.warmup, stream)
     ev_avg_ms = float(np.mean(ev))
@@ -315,7 +357,7 @@ def main():
     value = w.active_kv_bytes / (ms / 1e3) / 1e9
 
     dense = None
-    if not args.no_dense:
+    if not args.no_dense and not page:
         n_sel = w.H_kv if w.gqa else w.H
         dense_idx = torch.arange(n_sel, dtype=torch.int32, device=dev).repeat(w.B, 1)
         dn = sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, n_sel, w.gqa, q.dtype)
@@ -334,10 +376,11 @@ def main():
                  "ideal_speedup": n_sel / w.top_k}
 
     achieved = w.active_kv_bytes / (ev_avg_ms / 1e3) / 1e9
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name) if layout == "contig" else None
     out = {
-        "metric": METRIC if w.name == wl.HEADLINE else
-                  f"SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), {w.name}",
+        "metric": METRIC if (w.name == wl.HEADLINE and layout == "contig") else
+                  f"SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), {w.name}"
+                  + ("" if layout == "contig" else f", {layout} KV cache"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -353,7 +396,7 @@ def main():
         "data": "synthetic: i.i.d. N(0,1) q/k/v (seeded, drawn on device), seeded index rows",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d,
                    "Nkv": w.Nkv, "top_k": w.top_k, "gqa": w.gqa, "index_sampling": w.sampling,
-                   "nsplit": nsplit, "kv_copies_rotated": copies,
+                   "nsplit": nsplit, "kv_copies_rotated": copies, "kv_layout": layout,
                    "active_kv_bytes": w.active_kv_bytes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -367,7 +410,7 @@ def main():
                               if nsplit > 1 else "event span covers the one decode kernel")},
         "all_heads": dense,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and layout == "contig":
         out["cpu_baseline"] = cpu_baseline(w, q, ks[0], vs[0], idx, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

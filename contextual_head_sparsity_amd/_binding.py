@@ -21,8 +21,21 @@ _DT = {torch.float32: SHA_F32, torch.float16: SHA_F16, torch.bfloat16: SHA_BF16}
 STATUS = {0: "SHA_OK", 1: "SHA_ERR_INVALID_ARG", 2: "SHA_ERR_UNSUPPORTED",
           3: "SHA_ERR_MISALIGNED", 4: "SHA_ERR_WORKSPACE", 5: "SHA_ERR_HIP"}
 
+
+
+class KvLayout(ctypes.Structure):
+    """sha_kv_layout: element strides, per-row lengths and the page table."""
+    _fields_ = [("k_batch_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("k_row_stride", ctypes.c_int64), ("v_batch_stride", ctypes.c_int64),
+                ("v_head_stride", ctypes.c_int64), ("v_row_stride", ctypes.c_int64),
+                ("seqlens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("block_table_stride", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
 # (name, restype, argtypes) for every symbol include/sha.h declares.
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_L = ctypes.POINTER(KvLayout)
 _DECODE_ARGS = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P]
 SIGNATURES = {
     "sha_decode_f32": (_I, _DECODE_ARGS),
@@ -35,6 +48,9 @@ SIGNATURES = {
     "sha_decode_gqa": (_I, _DECODE_ARGS + [_I]),
     "sha_decode_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
     "sha_decode_gqa_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
+    "sha_decode_kv": (_I, _DECODE_ARGS + [_I, _L, _I, _P, _S]),
+    "sha_decode_gqa_kv": (_I, _DECODE_ARGS + [_I, _L, _I, _P, _S]),
+    "sha_workspace_bytes_kv": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _L]),
     "sha_plan_nsplit": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "sha_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
     "sha_mlp_union_workspace_bytes": (_S, [_I]),
@@ -90,22 +106,37 @@ def workspace_bytes(B, H, H_kv, Nkv, d, top_k, gqa=False, dtype=torch.float16, n
                                      num_cus)
 
 
-def _prepare(q, k, v, index, scale, out, gqa):
+def workspace_bytes_paged(B, H, H_kv, Nkv, d, top_k, gqa=False, dtype=torch.float16, nsplit=0,
+                          page_size=16, num_cus=0) -> int:
+    """Workspace of a paged call (its split geometry follows the page size).
+    Host-only query: the block-table address below is never dereferenced."""
+    n_pages = (Nkv + page_size - 1) // page_size
+    lay = KvLayout(0, 0, 8, 0, 0, 8)
+    lay.block_table, lay.block_table_stride, lay.page_size, lay.num_pages = 16, n_pages, page_size, 1
+    return lib().sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, int(gqa), _DT[dtype], nsplit,
+                                        num_cus, ctypes.byref(lay))
+
+
+def _prepare(q, k, v, index, scale, out, gqa, paged=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    for name, t in (("k", k), ("v", v)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be unit-stride")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one of float32 / float16 / bfloat16")
     B, H, one, d = q.shape
     if one != 1:
         raise ValueError("q must be [B, H, 1, d]")
     Bk, H_kv, Nkv, dk = k.shape
-    if (Bk, dk) != (B, d) or v.shape != k.shape:
-        raise ValueError("k, v must be [B, H_kv, Nkv, d] matching q")
+    if dk != d or v.shape != k.shape or (not paged and Bk != B):
+        raise ValueError("k, v must be [B, H_kv, Nkv, d] (paged: [num_pages, H_kv, page, d]) "
+                         "matching q")
     if index.dim() != 2 or index.shape[0] != B:
         raise ValueError("index must be [B, top_k]")
     if index.device != q.device:
@@ -124,38 +155,96 @@ def _prepare(q, k, v, index, scale, out, gqa):
     return B, H, H_kv, Nkv, d, top_k, index, float(scale), out
 
 
-def _call(gqa, q, k, v, index, scale, out, nsplit, workspace, stream):
-    B, H, H_kv, Nkv, d, top_k, index, scale, out = _prepare(q, k, v, index, scale, out, gqa)
+def _layout(k, v, seqlens, block_table, B, Nkv):
+    """KvLayout from the K/V views' strides (None for the plain contiguous call)."""
+    if seqlens is None and block_table is None and k.is_contiguous() and v.is_contiguous():
+        return None, ()
+    keep = []
+    lay = KvLayout(k.stride(0), k.stride(1), k.stride(2), v.stride(0), v.stride(1), v.stride(2))
+    if seqlens is not None:
+        seqlens = _dev_i32(seqlens, "seqlens")
+        if seqlens.numel() != B:
+            raise ValueError("seqlens must hold B entries")
+        lay.seqlens = seqlens.data_ptr()
+        keep.append(seqlens)
+    if block_table is not None:
+        bt = _dev_i32(block_table, "block_table")
+        if bt.dim() != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
+        lay.block_table = bt.data_ptr()
+        lay.block_table_stride = bt.shape[1]
+        lay.page_size = k.shape[2]
+        lay.num_pages = k.shape[0]
+        keep.append(bt)
+    return lay, keep
+
+
+def _call(gqa, q, k, v, index, scale, out, nsplit, workspace, stream, seqlens=None,
+          block_table=None, Nkv=None):
+    paged = block_table is not None
+    B, H, H_kv, Nk, d, top_k, index, scale, out = _prepare(q, k, v, index, scale, out, gqa, paged)
+    if paged:
+        if Nkv is None:
+            raise ValueError("a paged call needs Nkv (the longest row)")
+    else:
+        Nkv = Nk
+    lay, keep = _layout(k, v, seqlens, block_table, B, Nkv)
     L = lib()
     dt = _DT[q.dtype]
-    need = L.sha_workspace_bytes(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0)
+    lp = ctypes.byref(lay) if lay is not None else None
+    need = L.sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0, lp)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fn = L.sha_decode_gqa_ex if gqa else L.sha_decode_ex
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H, H_kv, Nkv, d,
-                top_k, scale, out.data_ptr(), stream.cuda_stream, dt, nsplit, ws_ptr, need)
-    _check(st, "sha_decode_gqa_ex" if gqa else "sha_decode_ex")
+        if lay is None:
+            name = "sha_decode_gqa_ex" if gqa else "sha_decode_ex"
+            st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H,
+                                  H_kv, Nkv, d, top_k, scale, out.data_ptr(), stream.cuda_stream,
+                                  dt, nsplit, ws_ptr, need)
+        else:
+            name = "sha_decode_gqa_kv" if gqa else "sha_decode_kv"
+            st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H,
+                                  H_kv, Nkv, d, top_k, scale, out.data_ptr(), stream.cuda_stream,
+                                  dt, lp, nsplit, ws_ptr, need)
+    del keep
+    _check(st, name)
     return out
 
 
 def sha_decode(q, k, v, batch_head_index, scale=None, out=None, nsplit=0, workspace=None,
-               stream=None):
+               stream=None, seqlens=None):
     """Head-indexed SHA decode; returns `out` (allocated zeroed when None).
 
-    q [B, H, 1, d], k/v [B, H_kv, Nkv, d], batch_head_index [B, top_k].
-    Slots of `out` not named by the index are left untouched.
+    q [B, H, 1, d] contiguous; k/v [B, H_kv, Nkv, d], any strides with a
+    unit-stride last dimension (e.g. a [B, Nkv, H_kv, d] cache viewed with
+    permute(0, 2, 1, 3)); batch_head_index [B, top_k]; seqlens [B] (optional)
+    limits row b to its first seqlens[b] keys.  Slots of `out` not named by
+    the index are left untouched.
     """
-    return _call(False, q, k, v, batch_head_index, scale, out, nsplit, workspace, stream)
+    return _call(False, q, k, v, batch_head_index, scale, out, nsplit, workspace, stream, seqlens)
 
 
 def sha_decode_gqa(q, k, v, batch_group_index, scale=None, out=None, nsplit=0, workspace=None,
-                   stream=None):
+                   stream=None, seqlens=None):
     """Group-indexed (GQA group sparsity) SHA decode; see sha_decode."""
-    return _call(True, q, k, v, batch_group_index, scale, out, nsplit, workspace, stream)
+    return _call(True, q, k, v, batch_group_index, scale, out, nsplit, workspace, stream, seqlens)
+
+
+def sha_decode_paged(q, k_pages, v_pages, block_table, index, Nkv, seqlens=None, gqa=False,
+                     scale=None, out=None, nsplit=0, workspace=None, stream=None):
+    """SHA decode over a paged cache.
+
+    k_pages / v_pages: [num_pages, H_kv, page_size, d] views of the page pool
+    (any strides, unit-stride last dimension; a [num_pages, page_size, H_kv,
+    d] pool is passed as pool.permute(0, 2, 1, 3)).  block_table [B,
+    max_pages] int32: row b's key r is on page block_table[b, r // page_size].
+    Nkv: the longest row; seqlens [B] optional.  gqa selects group indexing.
+    """
+    return _call(gqa, q, k_pages, v_pages, index, scale, out, nsplit, workspace, stream, seqlens,
+                 block_table, Nkv)
 
 
 # ---------------------------------------------------------------------------

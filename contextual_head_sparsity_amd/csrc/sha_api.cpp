@@ -28,6 +28,7 @@ struct Problem {
   float scale;
   int dtype;
   bool gqa;
+  const sha_kv_layout* kv;  // null: contiguous [B, H_kv, Nkv, d], every row Nkv keys
 };
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -114,19 +115,62 @@ int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int 
   return static_cast<int>(ns);
 }
 
-// Effective split geometry: `chunk` keys per split (a multiple of 16 keys
-// when there is more than one split), every split non-empty.
-void split_geometry(int Nkv, int nsplit_req, int* nsplit, int* chunk) {
+// Effective split geometry: `chunk` keys per split (a multiple of 16 keys,
+// and of the page size for a paged cache, when there is more than one
+// split), every split non-empty.  A paged cache (page > 0) also keeps every
+// split within sha::kMaxSplitPages pages, the page ids a workgroup stages.
+void split_geometry(int Nkv, int nsplit_req, int page, int* nsplit, int* chunk) {
   int ns = nsplit_req < 1 ? 1 : (nsplit_req > Nkv ? Nkv : nsplit_req);
+  if (page > 0) {
+    const long long span = static_cast<long long>(sha::kMaxSplitPages) * page;
+    const int min_ns = static_cast<int>((Nkv + span - 1) / span);
+    if (ns < min_ns) ns = min_ns;
+  }
   if (ns == 1) {
     *nsplit = 1;
     *chunk = Nkv;
     return;
   }
+  const int align = page > 16 ? page : 16;
   int c = (Nkv + ns - 1) / ns;
-  c = (c + 15) / 16 * 16;
+  c = (c + align - 1) / align * align;
   *chunk = c;
   *nsplit = (Nkv + c - 1) / c;
+}
+
+// KV layout checks.  Sets *kind (sha::KvLayout) and *page (rows per page, 0
+// unless paged).  A strided layout whose strides are the contiguous ones
+// runs as contiguous.
+sha_status check_kv(const sha_kv_layout* L, int H_kv, int Nkv, int d, int dtype, int* kind,
+                    int* page) {
+  *kind = sha::kKvContig;
+  *page = 0;
+  if (!L) return SHA_OK;
+  const int64_t unit = dtype == SHA_F32 ? 4 : 8;  // elements per 16 bytes
+  const int64_t st[6] = {L->k_batch_stride, L->k_head_stride, L->k_row_stride,
+                         L->v_batch_stride, L->v_head_stride, L->v_row_stride};
+  for (int64_t x : st) {
+    if (x < 0 || x > (int64_t(1) << 40)) return SHA_ERR_INVALID_ARG;
+    if (x % unit != 0) return SHA_ERR_MISALIGNED;
+  }
+  if (L->seqlens && !aligned(L->seqlens, 4)) return SHA_ERR_MISALIGNED;
+  if (L->block_table) {
+    const int P = L->page_size;
+    if (P < 16 || P > 65536 || (P & (P - 1)) != 0) return SHA_ERR_INVALID_ARG;
+    if (L->num_pages < 1) return SHA_ERR_INVALID_ARG;
+    if (L->block_table_stride < (Nkv + P - 1) / P) return SHA_ERR_INVALID_ARG;
+    if (!aligned(L->block_table, 4)) return SHA_ERR_MISALIGNED;
+    const long long span = static_cast<long long>(sha::kMaxSplitPages) * P;
+    if ((Nkv + span - 1) / span > kMaxSplits) return SHA_ERR_UNSUPPORTED;
+    *kind = sha::kKvPaged;
+    *page = P;
+    return SHA_OK;
+  }
+  const int64_t rs = d, hs = static_cast<int64_t>(Nkv) * d, bs = hs * H_kv;
+  const bool contig = L->k_batch_stride == bs && L->k_head_stride == hs && L->k_row_stride == rs &&
+                      L->v_batch_stride == bs && L->v_head_stride == hs && L->v_row_stride == rs;
+  *kind = contig ? sha::kKvContig : sha::kKvStrided;
+  return SHA_OK;
 }
 
 size_t partial_bytes(int B, int H, int H_kv, int d, int top_k, int gqa, int nsplit) {
@@ -150,7 +194,7 @@ sha_status run_auto(const Problem& p, hipStream_t stream) {
   if (st != SHA_OK || empty) return st;
   const int ns_plan = plan_nsplit(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, 0);
   int ns = 1, chunk = p.Nkv;
-  split_geometry(p.Nkv, ns_plan, &ns, &chunk);
+  split_geometry(p.Nkv, ns_plan, 0, &ns, &chunk);
   const bool gqa_eff = p.gqa && p.H / p.H_kv > 1;
   const size_t need = partial_bytes(p.B, p.H, p.H_kv, p.d, p.top_k, gqa_eff, ns);
   if (need == 0) return run(p, ns, nullptr, 0, stream);
@@ -193,13 +237,16 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   if (!aligned(p.q, 16) || !aligned(p.k, 16) || !aligned(p.v, 16) || !aligned(p.o, 16) ||
       !aligned(p.idx, 4))
     return SHA_ERR_MISALIGNED;
+  int kind = sha::kKvContig, page = 0;
+  st = check_kv(p.kv, p.H_kv, p.Nkv, p.d, p.dtype, &kind, &page);
+  if (st != SHA_OK) return st;
 
   const bool gqa_eff = p.gqa && p.H / p.H_kv > 1;
   int ns = 1, chunk = p.Nkv;
   const int req = nsplit_req > 0
                       ? nsplit_req
                       : plan_nsplit(p.B, p.H, p.H_kv, p.Nkv, p.d, p.top_k, p.gqa, p.dtype, 0);
-  split_geometry(p.Nkv, req, &ns, &chunk);
+  split_geometry(p.Nkv, req, page, &ns, &chunk);
 
   // Grid limit: blocks * threads per block (at most 512) must fit 32 bits.
   const long long blocks = wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa, p.dtype) * ns;
@@ -220,6 +267,22 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   a.nsplit = ns;
   a.chunk = chunk;
   a.scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
+  a.layout = kind;
+  if (p.kv) {
+    a.k_bs = p.kv->k_batch_stride;
+    a.k_hs = p.kv->k_head_stride;
+    a.k_rs = p.kv->k_row_stride;
+    a.v_bs = p.kv->v_batch_stride;
+    a.v_hs = p.kv->v_head_stride;
+    a.v_rs = p.kv->v_row_stride;
+    a.seqlens = p.kv->seqlens;
+    if (kind == sha::kKvPaged) {
+      a.block_table = p.kv->block_table;
+      a.bt_stride = p.kv->block_table_stride;
+      a.page_shift = __builtin_ctz(static_cast<unsigned>(page));
+      a.num_pages = p.kv->num_pages;
+    }
+  }
 
   const size_t need = partial_bytes(p.B, p.H, p.H_kv, p.d, p.top_k, gqa_eff, ns);
   if (need > 0) {
@@ -303,8 +366,9 @@ sha_status check_mlp(int B, int d, int D, int n_max, int dtype) {
 }
 
 Problem make(const void* q, const void* k, const void* v, const int32_t* idx, int B, int H,
-             int H_kv, int Nkv, int d, int top_k, float scale, void* o, int dtype, bool gqa) {
-  return Problem{q, k, v, idx, o, B, H, H_kv, Nkv, d, top_k, scale, dtype, gqa};
+             int H_kv, int Nkv, int d, int top_k, float scale, void* o, int dtype, bool gqa,
+             const sha_kv_layout* kv = nullptr) {
+  return Problem{q, k, v, idx, o, B, H, H_kv, Nkv, d, top_k, scale, dtype, gqa, kv};
 }
 
 }  // namespace
@@ -389,24 +453,55 @@ sha_status sha_decode_gqa_ex(const void* q, const void* k, const void* v,
              nsplit, workspace, workspace_bytes, stream);
 }
 
+sha_status sha_decode_kv(const void* q, const void* k, const void* v,
+                         const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv, int d,
+                         int top_k, float scale, void* o, hipStream_t stream, sha_dtype dtype,
+                         const sha_kv_layout* layout, int nsplit, void* workspace,
+                         size_t workspace_bytes) {
+  if (nsplit < 0) return SHA_ERR_INVALID_ARG;
+  return run(make(q, k, v, batch_head_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype, false,
+                  layout),
+             nsplit, workspace, workspace_bytes, stream);
+}
+
+sha_status sha_decode_gqa_kv(const void* q, const void* k, const void* v,
+                             const int32_t* batch_group_index, int B, int H, int H_kv, int Nkv,
+                             int d, int top_k, float scale, void* o, hipStream_t stream,
+                             sha_dtype dtype, const sha_kv_layout* layout, int nsplit,
+                             void* workspace, size_t workspace_bytes) {
+  if (nsplit < 0) return SHA_ERR_INVALID_ARG;
+  return run(make(q, k, v, batch_group_index, B, H, H_kv, Nkv, d, top_k, scale, o, dtype, true,
+                  layout),
+             nsplit, workspace, workspace_bytes, stream);
+}
+
 int sha_plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, sha_dtype dtype,
                     int num_cus) {
   bool empty = false;
   if (check_scalars(B, H, H_kv, Nkv, d, top_k, gqa, dtype, &empty) != SHA_OK) return 0;
   if (empty) return 1;
   int ns = 1, chunk = Nkv;
-  split_geometry(Nkv, plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus), &ns, &chunk);
+  split_geometry(Nkv, plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus), 0, &ns,
+                 &chunk);
   return ns;
+}
+
+size_t sha_workspace_bytes_kv(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
+                              sha_dtype dtype, int nsplit, int num_cus,
+                              const sha_kv_layout* layout) {
+  bool empty = false;
+  if (check_scalars(B, H, H_kv, Nkv, d, top_k, gqa, dtype, &empty) != SHA_OK || empty) return 0;
+  int kind = sha::kKvContig, page = 0;
+  if (check_kv(layout, H_kv, Nkv, d, dtype, &kind, &page) != SHA_OK) return 0;
+  const int req = nsplit > 0 ? nsplit : plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus);
+  int ns = 1, chunk = Nkv;
+  split_geometry(Nkv, req, page, &ns, &chunk);
+  return partial_bytes(B, H, H_kv, d, top_k, gqa && H / H_kv > 1, ns);
 }
 
 size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
                            sha_dtype dtype, int nsplit, int num_cus) {
-  bool empty = false;
-  if (check_scalars(B, H, H_kv, Nkv, d, top_k, gqa, dtype, &empty) != SHA_OK || empty) return 0;
-  const int req = nsplit > 0 ? nsplit : plan_nsplit(B, H, H_kv, Nkv, d, top_k, gqa, dtype, num_cus);
-  int ns = 1, chunk = Nkv;
-  split_geometry(Nkv, req, &ns, &chunk);
-  return partial_bytes(B, H, H_kv, d, top_k, gqa && H / H_kv > 1, ns);
+  return sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, gqa, dtype, nsplit, num_cus, nullptr);
 }
 
 size_t sha_mlp_union_workspace_bytes(int D) {

@@ -120,5 +120,67 @@ __device__ __forceinline__ uint4 ld16_stream(const char* p) {
                             __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p)));
 }
 
+// Keys row b holds: seqlens[b] clamped to [0, Nkv], or Nkv without seqlens.
+__device__ __forceinline__ int row_keys(const Args& a, int b) {
+  if (!a.seqlens) return a.Nkv;
+  return min(max(a.seqlens[b], 0), a.Nkv);
+}
+
+// Row addressing of one (batch row b, KV head g) stream for a workgroup whose
+// keys are [ks, ke).  k(r) / v(r) return the first byte of key row r; callers
+// add their column offset.  The paged form stages the page ids of [ks, ke)
+// in LDS (`pages`, kMaxSplitPages entries) and synchronises the workgroup,
+// so init() must be reached by every thread of the workgroup.
+template <int LAYOUT, int ROWB, int ES>
+struct KvRows {
+  const char* kb;
+  const char* vb;
+  long long krs, vrs;   // row strides in bytes (strided / paged)
+  long long kps, vps;   // page strides in bytes (paged)
+  const int* pages;
+  int ps, pm, p0;
+
+  __device__ __forceinline__ void init(const Args& a, int b, int g, int ks, int ke, int* lds_pages) {
+    const char* k = static_cast<const char*>(a.k);
+    const char* v = static_cast<const char*>(a.v);
+    if constexpr (LAYOUT == kKvContig) {
+      const size_t slab = (static_cast<size_t>(b) * a.H_kv + g) * static_cast<size_t>(a.Nkv) * ROWB;
+      kb = k + slab;
+      vb = v + slab;
+    } else if constexpr (LAYOUT == kKvStrided) {
+      kb = k + (b * a.k_bs + g * a.k_hs) * ES;
+      vb = v + (b * a.v_bs + g * a.v_hs) * ES;
+      krs = a.k_rs * ES;
+      vrs = a.v_rs * ES;
+    } else {
+      kb = k + g * a.k_hs * ES;
+      vb = v + g * a.v_hs * ES;
+      krs = a.k_rs * ES;
+      vrs = a.v_rs * ES;
+      kps = a.k_bs * ES;
+      vps = a.v_bs * ES;
+      ps = a.page_shift;
+      pm = (1 << a.page_shift) - 1;
+      p0 = ks >> a.page_shift;
+      const int n = ke > ks ? ((ke - 1) >> a.page_shift) - p0 + 1 : 0;
+      const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.bt_stride + p0;
+      for (int i = threadIdx.x; i < n; i += blockDim.x)
+        lds_pages[i] = min(max(bt[i], 0), a.num_pages - 1);
+      pages = lds_pages;
+      __syncthreads();
+    }
+  }
+  __device__ __forceinline__ const char* k(int r) const {
+    if constexpr (LAYOUT == kKvContig) return kb + static_cast<size_t>(r) * ROWB;
+    else if constexpr (LAYOUT == kKvStrided) return kb + r * krs;
+    else return kb + pages[(r >> ps) - p0] * kps + (r & pm) * krs;
+  }
+  __device__ __forceinline__ const char* v(int r) const {
+    if constexpr (LAYOUT == kKvContig) return vb + static_cast<size_t>(r) * ROWB;
+    else if constexpr (LAYOUT == kKvStrided) return vb + r * vrs;
+    else return vb + pages[(r >> ps) - p0] * vps + (r & pm) * vrs;
+  }
+};
+
 }  // namespace detail
 }  // namespace sha

@@ -117,8 +117,9 @@ constexpr int kTileKeys = 32;   // keys per wave tile (K of the PV product)
 constexpr int kCols = 16;       // query heads per workgroup (N of both products)
 
 // blockIdx.x = (unit * nchunk + chunk) * nsplit + split; the workgroup
-// computes query heads g*G + chunk*16 + c (c < 16) of group g.
-template <int DT, int D, int WAVES>
+// computes query heads g*G + chunk*16 + c (c < 16) of group g.  A split
+// holding none of row b's keys leaves (m, l, o) = (-inf, 0, 0).
+template <int DT, int D, int WAVES, int LAYOUT>
 __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a) {
   using M = Mma<DT>;
   constexpr int KC = D / 32;                 // d chunks of the QK product
@@ -131,6 +132,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   static_assert(kCols * D * 4 + kCols * 2 * 4 <= VBUF, "partial O must fit the V buffer");
 
   __shared__ __attribute__((aligned(16))) char smem[WAVES * VBUF];
+  __shared__ int sm_pages[LAYOUT == kKvPaged ? kMaxSplitPages : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -148,11 +150,10 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   const int nh = min(kCols, a.G - head0);
 
   const int ks = split * a.chunk;
-  const int ke = min(ks + a.chunk, a.Nkv);
+  const int ke = min(ks + a.chunk, row_keys(a, b));
 
-  const size_t slab = (static_cast<size_t>(b) * a.H_kv + g) * static_cast<size_t>(a.Nkv) * ROWB;
-  const char* kbase = static_cast<const char*>(a.k) + slab;
-  const char* vbase = static_cast<const char*>(a.v) + slab;
+  KvRows<LAYOUT, ROWB, 2> rows;
+  rows.init(a, b, g, ks, ke, sm_pages);
 
   // Q^T operands: head col, d = 32*kc + 8*q4 .. +8 (zero for heads past the group).
   uint4 qb[KC];
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
       if (!full) row = min(row, ke - 1);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kr[mb][kc] = ld16_stream(kbase + static_cast<size_t>(row) * ROWB + kc * 64 + q4 * 16);
+        kr[mb][kc] = ld16_stream(rows.k(row) + kc * 64 + q4 * 16);
     }
     // V tile: 1 KiB contiguous per wave load.
     uint4 vr[VLD];
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
     for (int u = 0; u < VLD; ++u) {
       int row = base + u * (1024 / ROWB) + lane / LPRW;
       if (!full) row = min(row, ke - 1);
-      vr[u] = ld16_stream(vbase + static_cast<size_t>(row) * ROWB + (lane % LPRW) * 16);
+      vr[u] = ld16_stream(rows.v(row) + (lane % LPRW) * 16);
     }
 
     // Scores S^T = K Q^T: lane holds keys 16*mb + 4*q4 + r of head col.
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
     }
     const int h = g * a.G + head0 + j;
     if (a.nsplit == 1) {
-      Elem<DT>::store(a.o, (static_cast<size_t>(b) * a.H + h) * D + c, accv / L);
+      Elem<DT>::store(a.o, (static_cast<size_t>(b) * a.H + h) * D + c, L > 0.f ? accv / L : 0.f);
     } else {
       const size_t pi = (static_cast<size_t>(unit) * a.G + head0 + j) * a.nsplit + split;
       a.part_o[pi * D + c] = accv;
@@ -302,9 +303,13 @@ template <int DT, int D>
 hipError_t launch_t(const Args& a, hipStream_t st) {
   constexpr int WAVES = 4;
   const unsigned nchunk = (a.G + kCols - 1) / kCols;
-  const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * nchunk * a.nsplit;
-  hipLaunchKernelGGL((sha_decode_gqa_mfma_kernel<DT, D, WAVES>), dim3(blocks), dim3(WAVES * 64),
-                     0, st, a);
+  const dim3 grid(static_cast<unsigned>(a.B) * a.top_k * nchunk * a.nsplit), block(WAVES * 64);
+  if (a.layout == kKvStrided)
+    hipLaunchKernelGGL((sha_decode_gqa_mfma_kernel<DT, D, WAVES, kKvStrided>), grid, block, 0, st, a);
+  else if (a.layout == kKvPaged)
+    hipLaunchKernelGGL((sha_decode_gqa_mfma_kernel<DT, D, WAVES, kKvPaged>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((sha_decode_gqa_mfma_kernel<DT, D, WAVES, kKvContig>), grid, block, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.nsplit > 1) e = launch_combine(a, DT, D, 1, st);
   return e;

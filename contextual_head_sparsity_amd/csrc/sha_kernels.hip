@@ -45,8 +45,8 @@ using namespace detail;
 // One iteration of a lane group's online softmax over U key rows
 // (rows r0, r0 + RSTEP, ...).  MASK handles the ragged last iteration: rows at
 // or beyond ke get score -inf and their (clamped, in-bounds) loads are unused.
-template <int DT, int LPR, int RSTEP, int U, int ROWB, bool MASK, int NH>
-__device__ __forceinline__ void online_step(const char* kp, const char* vp, const uint4 (&qv)[NH],
+template <int DT, int LPR, int RSTEP, int U, bool MASK, int NH, class Rows>
+__device__ __forceinline__ void online_step(const Rows& rows, int col, const uint4 (&qv)[NH],
                                             int r0, int ke, float sl2, float (&m)[NH],
                                             float (&l)[NH],
                                             float (&o)[NH][Elem<DT>::VEC]) {
@@ -56,12 +56,12 @@ __device__ __forceinline__ void online_step(const char* kp, const char* vp, cons
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
-    kr[u] = ld16_stream(kp + static_cast<size_t>(r) * ROWB);
+    kr[u] = ld16_stream(rows.k(r) + col);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int r = MASK ? min(r0 + u * RSTEP, ke - 1) : r0 + u * RSTEP;
-    vr[u] = ld16_stream(vp + static_cast<size_t>(r) * ROWB);
+    vr[u] = ld16_stream(rows.v(r) + col);
   }
   float s[NH][U];
 #pragma unroll
@@ -121,7 +121,10 @@ __device__ __forceinline__ void merge_wave(float (&m)[NH], float (&l)[NH], float
 
 // Shared body of the head kernel (NH = 1) and the group kernel (NH heads of
 // one KV group).  heads[j] < 0 marks an unused head slot of the last chunk.
-template <int DT, int D, int WAVES, int U, int NH>
+// A split that holds none of row b's keys (a short row) leaves m = -inf,
+// l = 0, o = 0: the merges give it zero weight and a row with no keys at all
+// gets zeros.
+template <int DT, int D, int WAVES, int U, int NH, int LAYOUT>
 __device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, int b, int g,
                                             const int (&heads)[NH], int part_head0,
                                             int part_heads) {
@@ -136,18 +139,18 @@ __device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, 
 
   __shared__ float sm_o[WAVES][NH][D];
   __shared__ float sm_ml[WAVES][NH][2];
+  __shared__ int sm_pages[LAYOUT == kKvPaged ? kMaxSplitPages : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPR, sub = lane % LPR;
 
   const int ks = split * a.chunk;
-  const int ke = min(ks + a.chunk, a.Nkv);
+  const int ke = min(ks + a.chunk, row_keys(a, b));
 
-  const size_t kv_off =
-      ((static_cast<size_t>(b) * a.H_kv + g) * static_cast<size_t>(a.Nkv)) * D + sub * VEC;
-  const char* kp = static_cast<const char*>(a.k) + kv_off * ES;
-  const char* vp = static_cast<const char*>(a.v) + kv_off * ES;
+  KvRows<LAYOUT, ROWB, ES> rows;
+  rows.init(a, b, g, ks, ke, sm_pages);
+  const int col = sub * VEC * ES;
 
   uint4 qv[NH];
 #pragma unroll
@@ -171,9 +174,9 @@ __device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, 
   int base = ks;
   const int nfull = (ke - ks) / RITER;
   for (int it = 0; it < nfull; ++it, base += RITER)
-    online_step<DT, LPR, RSTEP, U, ROWB, false, NH>(kp, vp, qv, base + lrow, ke, a.scale_log2, m, l, o);
+    online_step<DT, LPR, RSTEP, U, false, NH>(rows, col, qv, base + lrow, ke, a.scale_log2, m, l, o);
   if (base < ke)
-    online_step<DT, LPR, RSTEP, U, ROWB, true, NH>(kp, vp, qv, base + lrow, ke, a.scale_log2, m, l, o);
+    online_step<DT, LPR, RSTEP, U, true, NH>(rows, col, qv, base + lrow, ke, a.scale_log2, m, l, o);
 
   merge_wave<LPR, VEC, NH>(m, l, o);
 
@@ -208,7 +211,7 @@ __device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, 
       acc += wt * sm_o[w][j][c];
     }
     if (a.nsplit == 1) {
-      E::store(a.o, (static_cast<size_t>(b) * a.H + heads[j]) * D + c, acc / L);
+      E::store(a.o, (static_cast<size_t>(b) * a.H + heads[j]) * D + c, L > 0.f ? acc / L : 0.f);
     } else {
       const size_t p = (static_cast<size_t>(unit) * part_heads + part_head0 + j) * a.nsplit + split;
       a.part_o[p * D + c] = acc;
@@ -221,19 +224,19 @@ __device__ __forceinline__ void decode_unit(const Args& a, int unit, int split, 
 }
 
 // Head-indexed unit: blockIdx.x = unit * nsplit + split.
-template <int DT, int D, int WAVES, int U>
+template <int DT, int D, int WAVES, int U, int LAYOUT>
 __global__ __launch_bounds__(WAVES * 64) void sha_decode_mha_kernel(Args a) {
   const int split = blockIdx.x % a.nsplit;
   const int unit = blockIdx.x / a.nsplit;
   const int h = a.idx[unit];
   if (h < 0 || h >= a.H) return;  // padding / out-of-range entry: no read, no write
   const int heads[1] = {h};
-  decode_unit<DT, D, WAVES, U, 1>(a, unit, split, unit / a.top_k, h / a.G, heads, 0, 1);
+  decode_unit<DT, D, WAVES, U, 1, LAYOUT>(a, unit, split, unit / a.top_k, h / a.G, heads, 0, 1);
 }
 
 // Group-indexed unit: blockIdx.x = (unit * nchunk + chunk) * nsplit + split;
 // the workgroup computes query heads g*G + chunk*NH + j of group g.
-template <int DT, int D, int WAVES, int U, int NH>
+template <int DT, int D, int WAVES, int U, int NH, int LAYOUT>
 __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_kernel(Args a) {
   const int nchunk = (a.G + NH - 1) / NH;
   const int split = blockIdx.x % a.nsplit;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_kernel(Args a) {
     const int hj = chunk * NH + j;
     heads[j] = (hj < a.G) ? g * a.G + hj : -1;
   }
-  decode_unit<DT, D, WAVES, U, NH>(a, unit, split, unit / a.top_k, g, heads, chunk * NH, a.G);
+  decode_unit<DT, D, WAVES, U, NH, LAYOUT>(a, unit, split, unit / a.top_k, g, heads, chunk * NH, a.G);
 }
 
 // Merge the nsplit partials of one (unit, head): blockIdx.x = unit *
@@ -277,7 +280,9 @@ __global__ __launch_bounds__(D) void sha_combine_kernel(Args a, int gqa) {
     L += wt * a.part_ml[2 * (p0 + s) + 1];
     acc += wt * a.part_o[(p0 + s) * D + c];
   }
-  Elem<DT>::store(a.o, (static_cast<size_t>(unit / a.top_k) * a.H + h) * D + c, acc / L);
+  // L == 0: the row has no keys (every split empty); its output is zero.
+  Elem<DT>::store(a.o, (static_cast<size_t>(unit / a.top_k) * a.H + h) * D + c,
+                  L > 0.f ? acc / L : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -296,31 +301,35 @@ hipError_t launch_combine_t(const Args& a, int gqa, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DT, int D, int V>
+template <int DT, int D, int V, int LAYOUT = kKvContig>
 hipError_t launch_mha_v(const Args& a, hipStream_t st) {
   constexpr KernelShape s = kMhaShapes[V];
   const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * a.nsplit;
-  hipLaunchKernelGGL((sha_decode_mha_kernel<DT, D, s.waves, s.unroll>), dim3(blocks),
+  hipLaunchKernelGGL((sha_decode_mha_kernel<DT, D, s.waves, s.unroll, LAYOUT>), dim3(blocks),
                      dim3(s.waves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.nsplit > 1) e = launch_combine_t<DT, D>(a, 0, st);
   return e;
 }
 
-template <int DT, int D, int V, int NH>
+template <int DT, int D, int V, int NH, int LAYOUT = kKvContig>
 hipError_t launch_gqa_v(const Args& a, hipStream_t st) {
   constexpr KernelShape s = kGqaShapes[V];
   const unsigned nchunk = (a.G + NH - 1) / NH;
   const unsigned blocks = static_cast<unsigned>(a.B) * a.top_k * nchunk * a.nsplit;
-  hipLaunchKernelGGL((sha_decode_gqa_kernel<DT, D, s.waves, s.unroll, NH>), dim3(blocks),
+  hipLaunchKernelGGL((sha_decode_gqa_kernel<DT, D, s.waves, s.unroll, NH, LAYOUT>), dim3(blocks),
                      dim3(s.waves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.nsplit > 1) e = launch_combine_t<DT, D>(a, 1, st);
   return e;
 }
 
+// Strided and paged layouts run the default shape only; the tuning variants
+// exist for the contiguous layout.
 template <int DT, int D>
 hipError_t launch_mha_d(const Args& a, int variant, hipStream_t st) {
+  if (a.layout == kKvStrided) return launch_mha_v<DT, D, 0, kKvStrided>(a, st);
+  if (a.layout == kKvPaged) return launch_mha_v<DT, D, 0, kKvPaged>(a, st);
   switch (variant) {
     case 1: return launch_mha_v<DT, D, 1>(a, st);
     case 2: return launch_mha_v<DT, D, 2>(a, st);
@@ -335,6 +344,8 @@ hipError_t launch_mha_d(const Args& a, int variant, hipStream_t st) {
 
 template <int DT, int D, int NH>
 hipError_t launch_gqa_nh(const Args& a, int variant, hipStream_t st) {
+  if (a.layout == kKvStrided) return launch_gqa_v<DT, D, 0, NH, kKvStrided>(a, st);
+  if (a.layout == kKvPaged) return launch_gqa_v<DT, D, 0, NH, kKvPaged>(a, st);
   switch (variant) {
     case 1: return launch_gqa_v<DT, D, 1, NH>(a, st);
     case 2: return launch_gqa_v<DT, D, 2, NH>(a, st);

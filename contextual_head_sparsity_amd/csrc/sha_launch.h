@@ -9,11 +9,22 @@
 
 namespace sha {
 
+// How key/value rows are found in memory.
+//   kKvContig : [B, H_kv, Nkv, d] contiguous (compile-time row pitch).
+//   kKvStrided: row r of (b, g) at base + b*bs + g*hs + r*rs (element strides).
+//   kKvPaged  : row r of (b, g) on page block_table[b, r / P], at
+//               base + page*bs + g*hs + (r % P)*rs (bs is the page stride).
+enum KvLayout { kKvContig = 0, kKvStrided = 1, kKvPaged = 2 };
+
+// Page ids one workgroup stages in LDS for its key range (paged layout); the
+// host keeps every split within this many pages.
+constexpr int kMaxSplitPages = 1024;
+
 // Everything a launch needs, validated by the host before it gets here.
 struct Args {
   const void* q;        // [B, H, 1, d]
-  const void* k;        // [B, H_kv, Nkv, d]
-  const void* v;        // [B, H_kv, Nkv, d]
+  const void* k;        // keys, addressed as `layout` says
+  const void* v;        // values, addressed as `layout` says
   const int32_t* idx;   // [B, top_k]: head ids (MHA) or group ids (GQA)
   void* o;              // [B, H, 1, d]
   float* part_o;        // split partials: [units * heads_per_unit * nsplit, d] (unnormalised)
@@ -23,6 +34,15 @@ struct Args {
   int nsplit;           // effective split count (every split holds >= 1 key)
   int chunk;            // keys per split (last split may hold fewer)
   float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
+  // KV addressing (strided / paged layouts); strides in elements.
+  int layout;           // KvLayout
+  long long k_bs, k_hs, k_rs;
+  long long v_bs, v_hs, v_rs;
+  const int32_t* seqlens;      // [B] keys per row (clamped to [0, Nkv]) or null (all Nkv)
+  const int32_t* block_table;  // [B, bt_stride] page ids (paged)
+  int bt_stride;
+  int page_shift;              // log2(rows per page) (paged)
+  int num_pages;               // page ids are clamped into [0, num_pages) (paged)
 };
 
 enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };

@@ -156,6 +156,65 @@ sha_status sha_decode_gqa_ex(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes);
 
 /*
+ * KV cache layouts and per-row cache lengths.  A decode batch mixes requests
+ * whose caches hold different numbers of keys, and serving stacks keep the
+ * cache as [B, Nkv, H_kv, d], as per-head slabs, or in fixed-size pages.
+ * The pages run SHA inside such a decode loop (Polar Sparsity notes,
+ * papernotes.org, 实验关键数据: batched decoding throughput of full models);
+ * Algorithm 1 itself (reproducibility page, ri.k117.org, "Pseudocode") has
+ * one Nkv for every unit.  Row b attends to its first len_b =
+ * clamp(seqlens[b], 0, Nkv) keys; a row with len_b = 0 gets zeros in the
+ * selected slots.
+ *
+ *   Strided (block_table == NULL): key row r of batch row b, KV head g is at
+ *       k + (b * k_batch_stride + g * k_head_stride + r * k_row_stride) elements
+ *   (likewise v), so [B, Nkv, H_kv, d] has strides (Nkv*H_kv*d, d, H_kv*d).
+ *   Paged (block_table != NULL): rows are grouped in pages of page_size rows;
+ *       page p = block_table[b * block_table_stride + r / page_size],
+ *       k + (p * k_batch_stride + g * k_head_stride + (r % page_size) * k_row_stride)
+ *   i.e. k_batch_stride is the page stride of a pool of num_pages pages
+ *   (for a pool [num_pages, page_size, H_kv, d]: (page_size*H_kv*d, d, H_kv*d)).
+ *   Only the entries of pages that hold rows < len_b are read.  Page ids are
+ *   device data and are not checked on the host; an id outside
+ *   [0, num_pages) is clamped into that range (no out-of-pool read, but the
+ *   row's result is then meaningless).
+ * Every stride is >= 0 and a multiple of 16 bytes (16 / element-size
+ * elements), else SHA_ERR_MISALIGNED; page_size is a power of two in
+ * [16, 65536], block_table_stride >= ceil(Nkv / page_size) and
+ * num_pages >= 1, else SHA_ERR_INVALID_ARG.  seqlens (device int32 [B]) may
+ * be NULL: every row then holds Nkv keys.  A paged call keeps each KV split
+ * within 1024 pages (the split count is raised if needed; Nkv above
+ * 64 * 1024 * page_size is SHA_ERR_UNSUPPORTED).
+ */
+typedef struct sha_kv_layout {
+  int64_t k_batch_stride, k_head_stride, k_row_stride;
+  int64_t v_batch_stride, v_head_stride, v_row_stride;
+  const int32_t* seqlens;      /* [B] or NULL */
+  const int32_t* block_table;  /* [B, block_table_stride] or NULL (not paged) */
+  int32_t block_table_stride;
+  int32_t page_size;
+  int32_t num_pages;
+} sha_kv_layout;
+
+/*
+ * sha_decode_ex / sha_decode_gqa_ex over a caller-described KV layout
+ * (layout == NULL: the contiguous [B, H_kv, Nkv, d] layout, all rows Nkv
+ * keys).  q and o stay contiguous [B, H, 1, d].  Nkv is the longest row
+ * (the bound the split plan and seqlens clamp use).  The workspace is sized
+ * by sha_workspace_bytes_kv for the same arguments.
+ */
+sha_status sha_decode_kv(const void* q, const void* k, const void* v,
+                         const int32_t* batch_head_index, int B, int H, int H_kv, int Nkv,
+                         int d, int top_k, float scale, void* o, hipStream_t stream,
+                         sha_dtype dtype, const sha_kv_layout* layout, int nsplit,
+                         void* workspace, size_t workspace_bytes);
+sha_status sha_decode_gqa_kv(const void* q, const void* k, const void* v,
+                             const int32_t* batch_group_index, int B, int H, int H_kv,
+                             int Nkv, int d, int top_k, float scale, void* o,
+                             hipStream_t stream, sha_dtype dtype, const sha_kv_layout* layout,
+                             int nsplit, void* workspace, size_t workspace_bytes);
+
+/*
  * Launch planning (host only, no device work).
  *   sha_plan_nsplit    : the split count the library would use; num_cus <= 0
  *                        queries the current device's compute-unit count.
@@ -169,6 +228,10 @@ int sha_plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
                     sha_dtype dtype, int num_cus);
 size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
                            sha_dtype dtype, int nsplit, int num_cus);
+/* Workspace of sha_decode_kv / sha_decode_gqa_kv (layout may be NULL). */
+size_t sha_workspace_bytes_kv(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa,
+                              sha_dtype dtype, int nsplit, int num_cus,
+                              const sha_kv_layout* layout);
 
 /*
  * Attention router: the per-request active heads (or GQA groups) that feed

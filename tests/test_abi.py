@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -184,3 +184,64 @@ def test_router_host_validation():
     assert r(B=0, x=None, w=None, idx=None, sc=None) == 0
     assert r(sc=None) == 1 and r(idx=None) == 1
     assert r(x=P + 8) == 3 and r(idx=P + 2) == 3 and r(bias=P + 2) == 3
+
+
+def _kv_layout(**kw):
+    # contiguous [B, H_kv, Nkv, d] strides of ARGS (d = 64, Nkv = 64, H_kv = 4)
+    f = dict(k_batch_stride=4 * 64 * 64, k_head_stride=64 * 64, k_row_stride=64,
+             v_batch_stride=4 * 64 * 64, v_head_stride=64 * 64, v_row_stride=64)
+    f.update(kw)
+    return bd.KvLayout(**f)
+
+
+def _decode_kv(lay, fn="sha_decode_kv", dtype=1, nsplit=1, **kw):
+    a = dict(ARGS, **kw)
+    return getattr(bd.lib(), fn)(A16, A16, A16, A16, a["B"], a["H"], a["H_kv"], a["Nkv"], a["d"],
+                                 a["top_k"], 0.125, A16, None, dtype, ctypes.byref(lay), nsplit,
+                                 None, 0)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k_row_stride=4), 3),              # 8 bytes: rows not 16-byte aligned (f16)
+    (dict(v_head_stride=64 * 64 + 4), 3),
+    (dict(k_batch_stride=-64), 1),
+    (dict(seqlens=A16 + 2), 3),
+    (dict(block_table=A16, page_size=24, block_table_stride=4, num_pages=8), 1),   # not a power of 2
+    (dict(block_table=A16, page_size=8, block_table_stride=8, num_pages=8), 1),    # below 16
+    (dict(block_table=A16, page_size=16, block_table_stride=3, num_pages=8), 1),   # 64 keys need 4 pages
+    (dict(block_table=A16, page_size=16, block_table_stride=4, num_pages=0), 1),
+    (dict(block_table=A16 + 2, page_size=16, block_table_stride=4, num_pages=8), 3),
+])
+def test_kv_layout_validation(kw, expect):
+    assert _decode_kv(_kv_layout(**kw)) == expect
+    assert _decode_kv(_kv_layout(**kw), fn="sha_decode_gqa_kv", H=8, H_kv=4) == expect
+
+
+def test_kv_layout_limits_and_workspace():
+    L = bd.lib()
+    # f32 rows need 4-element (16-byte) strides; f16 needs 8 (the f32 case
+    # is checked through the workspace query, which launches nothing).
+    assert L.sha_workspace_bytes_kv(2, 4, 4, 64, 64, 2, 0, 0, 4, 256,
+                                    ctypes.byref(_kv_layout(k_row_stride=68))) > 0
+    assert L.sha_workspace_bytes_kv(2, 4, 4, 64, 64, 2, 0, 1, 4, 256,
+                                    ctypes.byref(_kv_layout(k_row_stride=68))) == 0
+    # Paged caches keep each split within 1024 pages: a 64-split cap.
+    huge = 64 * 1024 * 16 + 1
+    lay = _kv_layout(block_table=A16, page_size=16, block_table_stride=huge, num_pages=8)
+    assert _decode_kv(lay, Nkv=huge) == 2
+    # Paged split geometry: chunks are whole pages, and a row longer than
+    # 1024 pages forces a split even when one is requested.
+    lay = _kv_layout(block_table=A16, page_size=16, block_table_stride=2048, num_pages=8)
+    ws = L.sha_workspace_bytes_kv(2, 4, 4, 20000, 64, 2, 0, 1, 1, 256, ctypes.byref(lay))
+    n = 2 * 2 * 2
+    assert ws == (n * 64 * 4 + 255) // 256 * 256 + n * 8
+    lay = _kv_layout(block_table=A16, page_size=256, block_table_stride=16, num_pages=8)
+    ws = L.sha_workspace_bytes_kv(2, 4, 4, 4096, 64, 2, 0, 1, 5, 256, ctypes.byref(lay))
+    n = 2 * 2 * 4            # chunk 820 -> 1024 keys (4 pages): 4 splits
+    assert ws == (n * 64 * 4 + 255) // 256 * 256 + n * 8
+    # No layout: same accounting as sha_workspace_bytes.
+    assert L.sha_workspace_bytes_kv(4, 32, 32, 4096, 128, 16, 0, 1, 0, 256, None) == \
+        L.sha_workspace_bytes(4, 32, 32, 4096, 128, 16, 0, 1, 0, 256)
+    # Invalid layouts account to 0.
+    assert L.sha_workspace_bytes_kv(2, 4, 4, 64, 64, 2, 0, 1, 4, 256,
+                                    ctypes.byref(_kv_layout(k_row_stride=3))) == 0
