@@ -7,13 +7,13 @@ error: there is no CPU fallback.
 """
 from . import workloads
 
-__all__ = ["workloads", "sha_decode", "sha_decode_gqa", "sha_decode_paged", "lib", "mlp_union",
+__all__ = ["workloads", "sha_decode", "sha_decode_gqa", "sha_decode_paged", "DecodeStep", "lib", "mlp_union",
            "selective_mlp", "router_topk"]
 
 
 def __getattr__(name):
     if name in ("sha_decode", "sha_decode_gqa", "sha_decode_paged", "KvLayout", "lib",
-                "plan_nsplit", "workspace_bytes", "workspace_bytes_paged",
+                "plan_nsplit", "workspace_bytes", "workspace_bytes_paged", "DecodeStep",
                 "ShaError", "mlp_union", "selective_mlp", "selective_mlp_workspace_bytes",
                 "router_topk"):
         from . import _binding

@@ -33,6 +33,27 @@ class KvLayout(ctypes.Structure):
                 ("num_pages", ctypes.c_int32)]
 
 
+class StepConfig(ctypes.Structure):
+    """sha_step_config."""
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int),
+                ("Nkv", ctypes.c_int), ("d", ctypes.c_int), ("top_k", ctypes.c_int),
+                ("gqa", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("router_d", ctypes.c_int), ("mlp_d", ctypes.c_int), ("mlp_D", ctypes.c_int),
+                ("mlp_k", ctypes.c_int)]
+
+
+class StepLayer(ctypes.Structure):
+    """sha_step_layer."""
+    _fields_ = [("router_x", ctypes.c_void_p), ("router_w", ctypes.c_void_p),
+                ("router_bias", ctypes.c_void_p), ("router_scores", ctypes.c_void_p),
+                ("index", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("kv", ctypes.POINTER(KvLayout)), ("dense", ctypes.c_int),
+                ("mlp_x", ctypes.c_void_p), ("mlp_w1t", ctypes.c_void_p),
+                ("mlp_w2t", ctypes.c_void_p), ("mlp_y", ctypes.c_void_p),
+                ("mlp_rows", ctypes.c_void_p)]
+
+
 # (name, restype, argtypes) for every symbol include/sha.h declares.
 _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _L = ctypes.POINTER(KvLayout)
@@ -58,6 +79,10 @@ SIGNATURES = {
     "sha_selective_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "sha_selective_mlp": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _S]),
     "sha_router_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I]),
+    "sha_step_create": (_I, [ctypes.POINTER(StepConfig), ctypes.POINTER(StepLayer), _I, _I,
+                             ctypes.POINTER(ctypes.c_void_p)]),
+    "sha_step_run": (_I, [_P, _P]),
+    "sha_step_destroy": (_I, [_P]),
     "sha_status_string": (ctypes.c_char_p, [_I]),
     "sha_last_hip_error": (_I, []),
     "sha_version": (ctypes.c_char_p, []),
@@ -360,3 +385,72 @@ def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
                                    _DT[x.dtype])
     _check(st, "sha_router_topk")
     return index, scores
+
+
+# ---------------------------------------------------------------------------
+# multi-layer decode step (optionally one HIP graph)
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class DecodeStep:
+    """n layers of router -> selective head attention (-> selective MLP),
+    created once and run many times (sha_step_create / sha_step_run).
+
+    layers: list of dicts with device tensors under the sha_step_layer field
+    names (router_x, router_w, router_bias, router_scores, index, q, k, v, o,
+    dense, mlp_x, mlp_w1t, mlp_w2t, mlp_y, mlp_rows) and optionally
+    seqlens (per-row key counts; k/v must then be [B, H_kv, Nkv, d] views).
+    The tensors are referenced for the life of the step: refresh their
+    contents in place between runs.
+    """
+
+    def __init__(self, B, H, H_kv, Nkv, d, top_k, dtype, layers, gqa=False, scale=None,
+                 router_d=0, mlp_d=0, mlp_D=0, mlp_k=0, use_graph=True):
+        self._handle = None
+        self._keep = []
+        cfg = StepConfig(B, H, H_kv, Nkv, d, top_k, int(gqa),
+                         float(scale if scale is not None else 1.0 / math.sqrt(d)), _DT[dtype],
+                         router_d, mlp_d, mlp_D, mlp_k)
+        arr = (StepLayer * len(layers))()
+        for i, L in enumerate(layers):
+            for name in ("router_x", "router_w", "router_bias", "router_scores", "index", "q",
+                         "k", "v", "o", "mlp_x", "mlp_w1t", "mlp_w2t", "mlp_y", "mlp_rows"):
+                t = L.get(name)
+                if t is not None:
+                    if not t.is_cuda:
+                        raise ValueError(f"layer {i}: {name} must be a device tensor")
+                    self._keep.append(t)
+                setattr(arr[i], name, _ptr(t))
+            arr[i].dense = int(bool(L.get("dense", False)))
+            k, v, sl = L["k"], L["v"], L.get("seqlens")
+            if sl is not None or not (k.is_contiguous() and v.is_contiguous()):
+                lay, keep = _layout(k, v, sl, None, B, Nkv)
+                self._keep += [lay] + list(keep)
+                arr[i].kv = ctypes.pointer(lay)
+        self._keep.append(arr)
+        h = ctypes.c_void_p()
+        _check(lib().sha_step_create(ctypes.byref(cfg), arr, len(layers), int(use_graph),
+                                     ctypes.byref(h)), "sha_step_create")
+        self._handle = h
+
+    def run(self, stream=None):
+        if self._handle is None:
+            raise RuntimeError("step is closed")
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        _check(lib().sha_step_run(self._handle, stream.cuda_stream), "sha_step_run")
+
+    def close(self):
+        if self._handle is not None:
+            torch.cuda.synchronize()
+            lib().sha_step_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -48,9 +48,10 @@ def build(verbose: bool = True) -> str:
         _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
               os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    api = os.path.join(objdir, "sha_api.o")
-    _run([hipcc, "-c", *COMMON, os.path.join(CSRC, "sha_api.cpp"), "-o", api])
-    objs.append(api)
+    for src in ("sha_api.cpp", "sha_step.cpp"):
+        obj = os.path.join(objdir, src.replace(".cpp", ".o"))
+        _run([hipcc, "-c", *COMMON, os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)

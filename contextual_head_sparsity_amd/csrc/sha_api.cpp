@@ -373,6 +373,10 @@ Problem make(const void* q, const void* k, const void* v, const int32_t* idx, in
 
 }  // namespace
 
+namespace sha {
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace sha
+
 extern "C" {
 
 sha_status sha_decode(const void* q, const void* k, const void* v,

@@ -103,4 +103,7 @@ struct RouterArgs {
 
 hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t stream);
 
+// Records the hipError_t that sha_last_hip_error() reports on this thread.
+void set_last_hip_error(int e);
+
 }  // namespace sha

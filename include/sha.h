@@ -305,6 +305,74 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
                              hipStream_t stream, sha_dtype dtype, void* workspace,
                              size_t workspace_bytes);
 
+/*
+ * Multi-layer decode step.  The pages measure batched decoding throughput of
+ * whole models with the routers included, captured in CUDA graphs, and keep
+ * layer 0's attention dense because that layer's heads always matter most
+ * (Polar Sparsity notes, papernotes.org: 方法详解 > 关键设计 > "Attention Head
+ * 稀疏性", findings; 亮点与洞察, integration with CUDA Graphs; reproducibility
+ * page, ri.k117.org, "Software Dependencies").  A sha_step strings the sparse parts of one
+ * decode step together for n_layers layers, in order, on one stream:
+ *
+ *   sparse layer: sha_router_topk(router_x, router_w, router_bias) -> index
+ *                 sha_decode_kv / sha_decode_gqa_kv(q, k, v, index) -> o
+ *   dense layer : sha_decode_kv / sha_decode_gqa_kv over every head (group)
+ *   both, when mlp_w1t != NULL:
+ *                 sha_mlp_union(mlp_rows) -> S_B, sha_selective_mlp -> mlp_y
+ *
+ * and, with use_graph != 0, captures that sequence once into a HIP graph so
+ * that sha_step_run is a single graph launch.  The projections around these
+ * calls (QKV, output, the MLP router) are the caller's: the step reads its
+ * inputs from the pointers given here on every run, so a caller refreshes
+ * them in place between runs.  All pointers are device pointers owned by the
+ * caller and must stay valid until sha_step_destroy.  The step owns its
+ * workspaces (allocated in sha_step_create) and the dense index.
+ * Each layer's attention uses the library's split plan for the shared
+ * shape; cfg->top_k applies to sparse layers; a dense layer selects all H
+ * heads (H_kv groups when gqa != 0).
+ * Errors: any argument error of the underlying calls is returned by
+ * sha_step_create (nothing is captured or kept); SHA_ERR_HIP for a failing
+ * allocation, capture or launch.  Runs of one step must be ordered (they
+ * share its workspaces), and sha_step_destroy is called once the last run
+ * has finished (it frees the workspaces).  sha_step_create checks every
+ * call by capturing the sequence once (nothing executes); with
+ * use_graph == 0 the capture is kept only as that check and sha_step_run
+ * enqueues the calls one by one.
+ */
+typedef struct sha_step_config {
+  int B, H, H_kv, Nkv, d, top_k, gqa;
+  float scale;
+  sha_dtype dtype;
+  int router_d;          /* router input width */
+  int mlp_d, mlp_D, mlp_k;  /* selective MLP shape; mlp_k = neurons per row */
+} sha_step_config;
+
+typedef struct sha_step_layer {
+  const void* router_x;      /* [B, router_d] (sparse layers) */
+  const void* router_w;      /* [H or H_kv, router_d] */
+  const float* router_bias;  /* [H or H_kv] or NULL */
+  float* router_scores;      /* [B, H or H_kv] fp32 output (sparse layers) */
+  int32_t* index;            /* [B, top_k] router output (sparse layers; unused when dense) */
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const sha_kv_layout* kv;   /* NULL: contiguous; copied at create */
+  int dense;                 /* 1: all heads, no router */
+  const void* mlp_x;         /* [B, mlp_d] */
+  const void* mlp_w1t;       /* [mlp_D, mlp_d] or NULL (no MLP in this layer) */
+  const void* mlp_w2t;       /* [mlp_D, mlp_d] */
+  void* mlp_y;               /* [B, mlp_d] */
+  const int32_t* mlp_rows;   /* [B, mlp_k] */
+} sha_step_layer;
+
+typedef struct sha_step sha_step;
+
+sha_status sha_step_create(const sha_step_config* cfg, const sha_step_layer* layers, int n_layers,
+                           int use_graph, sha_step** step);
+sha_status sha_step_run(sha_step* step, hipStream_t stream);
+sha_status sha_step_destroy(sha_step* step);
+
 /* Human-readable name of a status code (static storage). */
 const char* sha_status_string(sha_status s);
 /* Raw hipError_t of the last SHA_ERR_HIP returned on the calling thread. */

@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 26, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -245,3 +245,29 @@ def test_kv_layout_limits_and_workspace():
     # Invalid layouts account to 0.
     assert L.sha_workspace_bytes_kv(2, 4, 4, 64, 64, 2, 0, 1, 4, 256,
                                     ctypes.byref(_kv_layout(k_row_stride=3))) == 0
+
+
+def test_step_host_validation():
+    """sha_step_create rejects bad configurations before any device work."""
+    L = bd.lib()
+    h = ctypes.c_void_p()
+
+    def create(n_layers=1, dense=0, index=A16, **kw):
+        cfg = dict(B=2, H=4, H_kv=4, Nkv=64, d=64, top_k=2, gqa=0, scale=0.125, dtype=1,
+                   router_d=64, mlp_d=0, mlp_D=0, mlp_k=0)
+        cfg.update(kw)
+        arr = (bd.StepLayer * max(n_layers, 1))()
+        for lay in arr:
+            lay.dense, lay.index, lay.router_scores = dense, index, A16
+        return L.sha_step_create(ctypes.byref(bd.StepConfig(**cfg)), arr, n_layers, 1,
+                                 ctypes.byref(h))
+
+    assert create(n_layers=0) == 1
+    assert create(B=0) == 1
+    assert create(top_k=0) == 1
+    assert create(H=4, H_kv=3) == 1          # invalid attention shape (planner says 0)
+    assert create(index=None) == 1           # a sparse layer needs its router output
+    assert h.value is None
+    assert L.sha_step_create(None, None, 1, 1, ctypes.byref(h)) == 1
+    assert L.sha_step_run(None, None) == 1
+    assert L.sha_step_destroy(None) == 1

@@ -1,0 +1,182 @@
+"""Multi-layer decode step on the GPU (sha_step_* through the C ABI).
+
+A step strings router -> selective head attention -> selective MLP over
+several layers, layer 0 dense, and may run as one captured HIP graph.  Every
+run is compared bit for bit with the same calls made one by one (each of
+those is pinned to the fp64 oracle by its own tests), and layer 0 is also
+checked against the oracle directly.  Graph replays are interleaved with
+in-place input updates, other device work and synchronisations, and every
+replay is checked.
+"""
+import numpy as np
+import pytest
+import torch
+
+import contextual_head_sparsity_amd as sha
+from contextual_head_sparsity_amd import workloads as wl
+from oracle import sha_decode_gqa_ref, sha_decode_ref
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_util import DEV, TOL, say
+
+
+def _gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _layers(cfg, n_layers, mlp, seed, seqlens_layer=None):
+    B, H, H_kv, d, Nkv = cfg["B"], cfg["H"], cfg["H_kv"], cfg["d"], cfg["Nkv"]
+    dt = cfg["dtype"]
+    nh = H_kv if cfg["gqa"] else H
+    g = _gen(seed)
+    out = []
+    for l in range(n_layers):
+        w = wl.Workload("step", B=B, H=H, H_kv=H_kv, d=d, Nkv=Nkv, top_k=cfg["top_k"],
+                        dtype=cfg["dname"], gqa=cfg["gqa"], seed=seed + l)
+        q, k, v = wl.make_qkv(w, DEV)
+        L = dict(q=q, k=k, v=v, o=wl.sentinel_like(w, DEV), dense=(l == 0))
+        if l == seqlens_layer:
+            L["k"] = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+            L["v"] = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+            L["seqlens"] = torch.randint(0, Nkv + 1, (B,), generator=g, device=DEV,
+                                         dtype=torch.int32)
+        if l > 0:
+            L["router_x"] = torch.randn(B, cfg["router_d"], generator=g, device=DEV).to(dt)
+            L["router_w"] = torch.randn(nh, cfg["router_d"], generator=g, device=DEV).to(dt)
+            L["router_bias"] = torch.randn(nh, generator=g, device=DEV)
+            L["router_scores"] = torch.empty(B, nh, device=DEV)
+            L["index"] = torch.empty(B, cfg["top_k"], dtype=torch.int32, device=DEV)
+        if mlp:
+            md, mD, mk = mlp
+            mw = wl.MlpWorkload("step", B=B, d=md, D=mD, k_row=mk, dtype=cfg["dname"],
+                                seed=seed + 100 + l)
+            x, w1t, w2t, rows = wl.make_mlp(mw, DEV)
+            L.update(mlp_x=x, mlp_w1t=w1t, mlp_w2t=w2t, mlp_rows=rows,
+                     mlp_y=torch.full_like(x, float("nan")))
+        out.append(L)
+    return out
+
+
+def _eager(cfg, layers, mlp):
+    """The step's calls one by one through the per-call entry points."""
+    B = cfg["B"]
+    nh = cfg["H_kv"] if cfg["gqa"] else cfg["H"]
+    fn = sha.sha_decode_gqa if cfg["gqa"] else sha.sha_decode
+    res = []
+    for L in layers:
+        r = {}
+        if L["dense"]:
+            idx = torch.arange(nh, dtype=torch.int32, device=DEV).repeat(B, 1)
+        else:
+            idx, sc = sha.router_topk(L["router_x"], L["router_w"], cfg["top_k"],
+                                      bias=L["router_bias"])
+            r["index"], r["router_scores"] = idx, sc
+        o = wl.sentinel_like(wl.Workload("s", B=B, H=cfg["H"], H_kv=cfg["H_kv"], d=cfg["d"],
+                                         Nkv=cfg["Nkv"], top_k=1, dtype=cfg["dname"]), DEV)
+        r["o"] = fn(L["q"], L["k"], L["v"], idx, scale=cfg["scale"], out=o,
+                    seqlens=L.get("seqlens"))
+        if mlp:
+            md, mD, mk = mlp
+            sel, n_sel = sha.mlp_union(L["mlp_rows"], mD)
+            r["mlp_y"] = sha.selective_mlp(L["mlp_x"], L["mlp_w1t"], L["mlp_w2t"], sel, n_sel,
+                                           n_max=min(B * mk, mD))
+        res.append(r)
+    torch.cuda.synchronize()
+    return res
+
+
+def _compare(layers, ref):
+    for l, (L, r) in enumerate(zip(layers, ref)):
+        for name, t in r.items():
+            got = L[name]
+            if got.dtype.is_floating_point:
+                same = torch.equal(wl.raw_bits(got) if got.dtype != torch.float32
+                                   else got.view(torch.int32),
+                                   wl.raw_bits(t) if t.dtype != torch.float32
+                                   else t.view(torch.int32))
+            else:
+                same = torch.equal(got, t)
+            assert same, f"layer {l}: {name} differs from the per-call result"
+
+
+def _reset_outputs(cfg, layers):
+    for L in layers:
+        L["o"].copy_(wl.sentinel_like(wl.Workload("s", B=cfg["B"], H=cfg["H"], H_kv=cfg["H_kv"],
+                                                  d=cfg["d"], Nkv=cfg["Nkv"], top_k=1,
+                                                  dtype=cfg["dname"]), DEV))
+        if "mlp_y" in L:
+            L["mlp_y"].fill_(float("nan"))
+        if "index" in L:
+            L["index"].fill_(-5)
+
+
+def _refresh_inputs(layers, seed):
+    g = _gen(seed)
+    for L in layers:
+        L["q"].copy_(torch.randn(L["q"].shape, generator=g, device=DEV).to(L["q"].dtype))
+        if "router_x" in L:
+            L["router_x"].copy_(torch.randn(L["router_x"].shape, generator=g, device=DEV)
+                                .to(L["router_x"].dtype))
+        if "mlp_x" in L:
+            L["mlp_x"].copy_(torch.randn(L["mlp_x"].shape, generator=g, device=DEV)
+                             .to(L["mlp_x"].dtype))
+            D = L["mlp_w1t"].shape[0]
+            L["mlp_rows"].copy_(torch.randint(-1, D, L["mlp_rows"].shape, generator=g,
+                                              device=DEV, dtype=torch.int32))
+
+
+CASES = {
+    "opt_mha_f16_mlp": (dict(B=8, H=8, H_kv=8, d=128, Nkv=300, top_k=3, gqa=False,
+                             dtype=torch.float16, dname="f16", router_d=256),
+                        (256, 1024, 64), None),
+    "gqa_bf16_ragged": (dict(B=4, H=16, H_kv=4, d=128, Nkv=700, top_k=2, gqa=True,
+                             dtype=torch.bfloat16, dname="bf16", router_d=512),
+                        None, 2),
+    "mha_f32_d64": (dict(B=3, H=6, H_kv=6, d=64, Nkv=2100, top_k=2, gqa=False,
+                         dtype=torch.float32, dname="f32", router_d=128),
+                    None, 1),
+}
+
+
+@pytest.mark.parametrize("use_graph", [True, False])
+@pytest.mark.parametrize("case", list(CASES))
+def test_step_matches_per_call(case, use_graph):
+    cfg, mlp, sl_layer = CASES[case]
+    cfg = dict(cfg, scale=1.0 / np.sqrt(cfg["d"]))
+    say(f"[step] {case} graph={use_graph}")
+    n_layers = 3
+    layers = _layers(cfg, n_layers, mlp, seed=17, seqlens_layer=sl_layer)
+    md, mD, mk = mlp if mlp else (0, 0, 0)
+    step = sha.DecodeStep(cfg["B"], cfg["H"], cfg["H_kv"], cfg["Nkv"], cfg["d"], cfg["top_k"],
+                          cfg["dtype"], layers, gqa=cfg["gqa"], scale=cfg["scale"],
+                          router_d=cfg["router_d"], mlp_d=md, mlp_D=mD, mlp_k=mk,
+                          use_graph=use_graph)
+    try:
+        for rep in range(3):
+            _reset_outputs(cfg, layers)
+            torch.cuda.synchronize()
+            step.run()
+            torch.cuda.synchronize()
+            ref = _eager(cfg, layers, mlp)
+            _compare(layers, ref)
+            if rep == 0:
+                # layer 0 is dense: every head written, equal to the oracle
+                L = layers[0]
+                ref_fn = sha_decode_gqa_ref if cfg["gqa"] else sha_decode_ref
+                nh = cfg["H_kv"] if cfg["gqa"] else cfg["H"]
+                idx = np.tile(np.arange(nh, dtype=np.int32), (cfg["B"], 1))
+                O, written = ref_fn(L["q"].cpu(), L["k"].cpu(), L["v"].cpu(), idx, cfg["scale"])
+                assert written.all()
+                err = float(np.max(np.abs(L["o"].cpu().double().numpy() - O)))
+                assert err <= TOL[cfg["dname"]], err
+            # in-place refresh plus unrelated device work before the next run
+            _refresh_inputs(layers, seed=100 + rep)
+            torch.cuda.synchronize()
+            junk = torch.randn(1 << 20, device=DEV).cumsum(0)
+            del junk
+    finally:
+        step.close()
