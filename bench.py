@@ -73,6 +73,11 @@ def parse():
     p.add_argument("--mlp", default=None, choices=list(wl.MLP_WORKLOADS),
                    help="measure the selective MLP on this workload instead of SHA decode")
     p.add_argument("--mlp-batch", type=int, default=0, help="override the MLP workload's B")
+    p.add_argument("--decode-step", type=int, default=0, metavar="L",
+                   help="time an L-layer decode step (router -> SHA -> selective MLP, layer 0 "
+                        "dense) as one HIP graph and call by call")
+    p.add_argument("--step-mlp", default=None, choices=list(wl.MLP_WORKLOADS),
+                   help="MLP shape inside the decode step (its dtype follows the workload)")
     return p.parse_args()
 
 
@@ -291,8 +296,67 @@ def to_pages(w, ks, vs, page, dev):
     return [pool(t) for t in ks], [pool(t) for t in vs], bt
 
 
+def bench_step(args):
+    """An L-layer decode step of the workload's attention shape: per layer the
+    attention router (layer 0: every head, no router), the selective head
+    attention and, with --step-mlp, the MLP union and selective MLP; timed
+    as one HIP graph launch and as the same calls made one by one."""
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dt = wl.DTYPES[w.dtype]
+    n_layers = args.decode_step
+    nh = w.H_kv if w.gqa else w.H
+    router_d = w.H * w.d
+    mw = None
+    if args.step_mlp:
+        mw = wl.MLP_WORKLOADS[args.step_mlp].with_(B=w.B, dtype=w.dtype)
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    layers = []
+    for l in range(n_layers):
+        q, k, v, idx, o = wl.make_workload(w.with_(seed=w.seed + 10 * l), dev)
+        L = dict(q=q, k=k, v=v, o=o, dense=(l == 0))
+        if l > 0:
+            L["router_x"] = torch.randn(w.B, router_d, generator=g, device=dev).to(dt)
+            L["router_w"] = (torch.randn(nh, router_d, generator=g, device=dev)
+                             / math.sqrt(router_d)).to(dt)
+            L["router_scores"] = torch.empty(w.B, nh, device=dev)
+            L["index"] = torch.empty(w.B, w.top_k, dtype=torch.int32, device=dev)
+        if mw is not None:
+            x, w1t, w2t, rows = wl.make_mlp(mw.with_(seed=mw.seed + l), dev)
+            L.update(mlp_x=x, mlp_w1t=w1t, mlp_w2t=w2t, mlp_rows=rows, mlp_y=torch.empty_like(x))
+        layers.append(L)
+    kw = dict(gqa=w.gqa, scale=w.scale, router_d=router_d,
+              mlp_d=mw.d if mw else 0, mlp_D=mw.D if mw else 0, mlp_k=mw.k_row if mw else 0)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for mode in ("graph", "eager"):
+        step = sha.DecodeStep(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, dt, layers,
+                              use_graph=(mode == "graph"), **kw)
+        ms, ev = time_calls(lambda i: step.run(stream), args.steps, args.warmup, stream)
+        res[mode] = {"us_per_step": round(ms * 1e3, 2), "event_us_per_step":
+                     round(float(np.mean(ev)) * 1e3, 2)}
+        step.close()
+    kv_bytes = w.active_kv_bytes * (n_layers - 1) + w.dense_kv_bytes
+    out = {
+        "metric": f"decode step of {n_layers} layers (router + SHA"
+                  + (" + selective MLP" if mw else "") + ", layer 0 dense), \u00b5s per step",
+        "value": res["graph"]["us_per_step"], "unit": "us", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) q/k/v, router and MLP weights",
+        "config": {"workload": w.name, "layers": n_layers, "mlp": args.step_mlp,
+                   "router_d": router_d},
+        "graph": res["graph"], "eager": res["eager"],
+        "attention_kv_bytes_per_step": kv_bytes,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.decode_step:
+        bench_step(args)
+        return
     if args.mlp:
         bench_mlp(args)
         return
