@@ -234,7 +234,7 @@ def bench_mlp(args):
     wsb = sha.selective_mlp_workspace_bytes(w.B, w.d, w.D, n_max)
     work = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
-    uws = torch.empty(w.D + 256, dtype=torch.uint8, device=dev)
+    uws = torch.empty(sha.lib().sha_mlp_union_workspace_bytes(w.D), dtype=torch.uint8, device=dev)
     sha.mlp_union(rows, w.D, sel=sel, n_sel=n_sel, workspace=uws)
     torch.cuda.synchronize()
     n = int(n_sel.item())

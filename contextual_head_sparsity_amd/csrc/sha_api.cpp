@@ -317,17 +317,44 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Grid sizes from the selection bound.  Both products stream weights, so the
 // planner fills the chip without leaving a small second round of work.
-// Residency from the kernels' register use on gfx950: the up projection's
-// waves (224 registers) fit 2 per SIMD, 8 per CU.
-//   up  : one wave per 64 selected neurons x 64 batch rows; its K (d) is
-//         split so that the waves fill the 8-per-CU slots once (at most 16
-//         splits).
+//   up  : one workgroup per 64 selected neurons x 64 batch rows (2 resident
+//         per CU); its K (d) is split in whole 256-k stages.  A grid that
+//         fills half to all of the resident slots runs unsplit; a smaller
+//         one is split until it fills about half of them (at most 8 ways); a
+//         larger one takes 2 or 3 splits, whichever gives the fewer rounds of
+//         resident workgroups per unit of work after the cost of the fp32
+//         partials each split writes and the finalize reads back.
 //   down: one workgroup per 256 output columns x 64 rows; the neuron range is
 //         split for about two workgroups per CU (each range keeps >= 64
 //         neurons, at most 64 splits).
-// The constants come from a split sweep of the OPT-66B MLP on MI355X.
-constexpr int kUpWavesPerCu = 8;
+// The constants come from split sweeps of the OPT MLPs on MI355X.
+constexpr int kUpWgsPerCu = 2;
 constexpr int kDownWgsPerCu = 2;
+
+int up_split_count(long long items, int kstages, int b_pad, int d, int cus) {
+  const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
+  int us = 1;
+  if (2 * items < slots) {
+    us = static_cast<int>(slots / (2 * items));
+    if (us > 8) us = 8;
+  } else if (items > slots) {
+    double best_cost = 0.0;
+    for (int cand = 2; cand <= 3; ++cand) {
+      const long long rounds = (items * cand + slots - 1) / slots;
+      // Unit: one round of full-K workgroups.  Partials: cand x (b_pad x n)
+      // fp32 written and read, against slots x 64 x d 16-bit weights per round.
+      const double partial = static_cast<double>(cand) * items * 64 * b_pad * 8 /
+                             (static_cast<double>(slots) * 64 * d * 2);
+      const double cost = static_cast<double>(rounds) / cand + partial;
+      if (cand == 2 || cost < best_cost) {
+        us = cand;
+        best_cost = cost;
+      }
+    }
+  }
+  if (us > kstages) us = kstages;
+  return us < 1 ? 1 : us;
+}
 
 MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   MlpPlan p{};
@@ -335,13 +362,11 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   p.n_pad = ((n_max > 0 ? n_max : 1) + 63) / 64 * 64;
   p.b_pad = (B + 63) / 64 * 64;
   const long long up_items = static_cast<long long>(p.n_pad / 64) * (p.b_pad / 64);
-  long long us = static_cast<long long>(kUpWavesPerCu) * cus / up_items;
-  const int kchunks = d / 128;
-  if (us > kchunks) us = kchunks;
-  if (us > 16) us = 16;
-  if (us < 1) us = 1;
+  const int kstages = d / 256;
+  int us = up_split_count(up_items, kstages, p.b_pad, d, cus);
   if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
-  p.up_kper = (kchunks + static_cast<int>(us) - 1) / static_cast<int>(us) * 128;
+  if (us > kstages) us = kstages;
+  p.up_kper = (kstages + us - 1) / us * 256;
   p.up_splits = (d + p.up_kper - 1) / p.up_kper;
   const long long dn_items = static_cast<long long>(d / 256) * (p.b_pad / 64);
   long long ds = static_cast<long long>(kDownWgsPerCu) * cus / dn_items;
@@ -509,7 +534,9 @@ size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, in
 }
 
 size_t sha_mlp_union_workspace_bytes(int D) {
-  return D < 1 ? 0 : round256(static_cast<size_t>(D));
+  if (D < 1) return 0;
+  return round256(static_cast<size_t>(D)) +
+         round256(static_cast<size_t>(sha::mlp_union_blocks(D)) * sizeof(int32_t));
 }
 
 sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_t* sel,
@@ -524,8 +551,10 @@ sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_
   if (!workspace || workspace_bytes < sha_mlp_union_workspace_bytes(D)) return SHA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
   (void)hipGetLastError();
+  uint8_t* flags = static_cast<uint8_t*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(flags + round256(static_cast<size_t>(D)));
   const hipError_t e = sha::launch_mlp_union(row_neurons, static_cast<int>(total), D, sel, n_sel,
-                                             static_cast<uint8_t*>(workspace), stream);
+                                             flags, counts, stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;
     return SHA_ERR_HIP;

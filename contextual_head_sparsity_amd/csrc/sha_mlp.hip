@@ -11,13 +11,15 @@
 // Kernels:
 //   union  - a flag byte per neuron in a workspace: cleared, marked by every
 //            row's entries (plain byte stores, any order gives the same flags),
-//            then one workgroup scans the flags and writes the marked neurons
-//            in ascending order and their count, on device (deterministic).
+//            counted per 4096-flag block, then every block writes its marked
+//            neurons in ascending order at the offset the earlier blocks'
+//            counts give, and the last block writes the total (deterministic,
+//            on device).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
-//            each wave owns 64 selected neurons x 64 batch rows over a K
-//            range and streams the selected weight rows straight into A
-//            operands (non-temporal 128-bit loads, 8 KiB per batch) with x
-//            pieces from L2 as B operands; no LDS, no barriers.  With one K
+//            a workgroup owns 64 selected neurons x 64 batch rows over a K
+//            range; weight rows stream in 512-byte runs (non-temporal
+//            128-bit loads, two stages ahead) through swizzled LDS into A
+//            operands, x pieces come from L2 as B operands.  With one K
 //            split it applies ReLU and writes H (16-bit); with several it
 //            writes fp32 partials and `up_finalize` sums them.
 //   down   - y = H W2t[S] on MFMA: a workgroup owns 64 batch rows x 256
@@ -31,6 +33,8 @@
 // and workgroups past the actual count exit or mask.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sha_device.h"
 #include "sha_launch.h"
@@ -91,8 +95,6 @@ struct Mx<kF16> {
 // ---------------------------------------------------------------------------
 // union of the rows' neuron lists: one flag byte per neuron in a workspace
 // ---------------------------------------------------------------------------
-constexpr int kUnionThreads = 1024;
-
 // flags[0 .. D) = 0 (16-byte stores; the flag buffer is padded to 256 bytes).
 __global__ __launch_bounds__(256) void sha_mlp_union_clear_kernel(uint8_t* flags, int D) {
   const int n16 = (D + 15) / 16;
@@ -110,54 +112,87 @@ __global__ __launch_bounds__(256) void sha_mlp_union_mark_kernel(const int32_t* 
   }
 }
 
-// One workgroup: exclusive scan of the flags in ascending neuron order, each
-// set flag writes its neuron id at its rank; the total goes to *n_sel.
-__global__ __launch_bounds__(kUnionThreads) void sha_mlp_union_compact_kernel(
-    const uint8_t* flags, int D, int32_t* sel, int32_t* n_sel) {
-  __shared__ uint32_t wave_sums[kUnionThreads / 64];
-  __shared__ uint32_t carry;
+// Compaction in two launches over blocks of kUnionBlockFlags flags (one
+// 16-flag word per thread): `count` stores each block's number of set flags;
+// `write` sums the counts of the blocks before its own (its output offset),
+// scans its words, gathers its neurons in LDS in ascending order and copies
+// them out with contiguous stores; the last block also stores the total.
+constexpr int kUnionBlockFlags = 4096;
+constexpr int kUnionBlockThreads = kUnionBlockFlags / 16;
+
+__device__ __forceinline__ uint32_t flag_count(uint4 f) {
+  return __popc(f.x & 0x01010101u) + __popc(f.y & 0x01010101u) + __popc(f.z & 0x01010101u) +
+         __popc(f.w & 0x01010101u);
+}
+
+// Inclusive sum over the workgroup's threads (kUnionBlockThreads = 4 waves).
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_sums, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry = 0u;
-  __syncthreads();
-  // each thread owns 16 consecutive flags per step
-  for (int base = 0; base < D; base += kUnionThreads * 16) {
-    const int j0 = base + tid * 16;
-    uint4 f = make_uint4(0, 0, 0, 0);
-    if (j0 < D) f = reinterpret_cast<const uint4*>(flags)[j0 / 16];
-    // flags past D in the last word are zero (cleared padding)
-    const uint32_t w[4] = {f.x, f.y, f.z, f.w};
-    uint32_t cnt = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cnt += __popc(w[q] & 0x01010101u);
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
-    if (lane == 63) wave_sums[wave] = incl;
-    __syncthreads();
-    uint32_t pos = carry;
-    for (int q = 0; q < wave; ++q) pos += wave_sums[q];
-    const uint32_t block_end = pos + incl;
-    pos += incl - cnt;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((w[q] >> (8 * e)) & 1u) sel[pos++] = j0 + 4 * q + e;
-    __syncthreads();
-    if (tid == kUnionThreads - 1) carry = block_end;
-    __syncthreads();
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-  if (tid == 0) *n_sel = static_cast<int32_t>(carry);
+  if (lane == 63) wave_sums[wave] = v;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int q = 0; q < kUnionBlockThreads / 64; ++q) {
+    const uint32_t ws = wave_sums[q];
+    if (q < wave) before += ws;
+    all += ws;
+  }
+  *total = all;
+  return v + before;
+}
+
+__global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_count_kernel(
+    const uint8_t* flags, int D, int32_t* counts) {
+  __shared__ uint32_t wave_sums[kUnionBlockThreads / 64];
+  const int word = blockIdx.x * kUnionBlockThreads + threadIdx.x;
+  const int n16 = (D + 15) / 16;   // flags past D in the last word are cleared zeros
+  const uint32_t c = word < n16 ? flag_count(reinterpret_cast<const uint4*>(flags)[word]) : 0u;
+  uint32_t total;
+  block_scan(c, wave_sums, &total);
+  if (threadIdx.x == 0) counts[blockIdx.x] = static_cast<int32_t>(total);
+}
+
+__global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_write_kernel(
+    const uint8_t* flags, int D, const int32_t* counts, int32_t* sel, int32_t* n_sel) {
+  __shared__ uint32_t wave_sums[kUnionBlockThreads / 64];
+  __shared__ int32_t staged[kUnionBlockFlags];
+  __shared__ uint32_t base_sh;
+  const int tid = threadIdx.x;
+  // Output offset of this block: the counts of the blocks before it.
+  uint32_t part = 0;
+  for (int q = tid; q < static_cast<int>(blockIdx.x); q += kUnionBlockThreads)
+    part += static_cast<uint32_t>(counts[q]);
+  uint32_t base;
+  block_scan(part, wave_sums, &base);
+  if (tid == 0) base_sh = base;
+  __syncthreads();  // wave_sums is reused below
+  base = base_sh;
+
+  const int word = blockIdx.x * kUnionBlockThreads + tid;
+  const int n16 = (D + 15) / 16;
+  const uint4 f = word < n16 ? reinterpret_cast<const uint4*>(flags)[word] : make_uint4(0, 0, 0, 0);
+  const uint32_t cnt = flag_count(f);
+  uint32_t n_block;
+  uint32_t pos = block_scan(cnt, wave_sums, &n_block) - cnt;
+  const uint32_t w[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((w[q] >> (8 * e)) & 1u) staged[pos++] = word * 16 + 4 * q + e;
+  __syncthreads();
+  for (uint32_t i = tid; i < n_block; i += kUnionBlockThreads) sel[base + i] = staged[i];
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) *n_sel = static_cast<int32_t>(base + n_block);
 }
 
 // ---------------------------------------------------------------------------
 // up projection: H = relu(x W1t[S]^T)
 // ---------------------------------------------------------------------------
-constexpr int kUpSteps = 2;   // MFMA K steps (of 32) per iteration: 8 KiB of weights in flight
-
 __device__ __forceinline__ int sel_count(const MlpArgs& a) {
   const int n = *a.n_sel;
   return n < 0 ? 0 : (n > a.n_max ? a.n_max : n);
@@ -175,93 +210,153 @@ __device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
   return r >= 0 && r < a.D;
 }
 
-// One wave owns 64 selected neurons (4 MFMA row blocks) x 64 batch rows
-// (4 column blocks) over a K range; waves are independent (no LDS, no
-// barriers), so a CU keeps several waves' 8 KiB weight batches in flight.
-// The x pieces (B operands) are re-read from L2 by every wave of the same K
-// range: as many bytes as the wave's weights.
-// Wave id = ((btile * up_splits) + split) * nblocks + nblock.
+// A workgroup owns 64 selected neurons x 64 batch rows over a K range, in
+// stages of kUpKc = 256 k.  Each stage's weights (64 rows x 512 B) are read
+// with 128-bit non-temporal loads, two rows of 512 contiguous bytes per wave
+// instruction, two stages ahead (three register sets in rotation), and
+// written to LDS with an XOR swizzle of the 16-byte pieces
+// (slot = piece ^ (row & 15)), so that the A-operand reads (16 rows x one
+// piece per quarter wave) hit distinct banks.  Wave w multiplies all 64
+// neurons by batch block w: its x pieces (B operands) come from L2 into
+// registers one stage ahead, and no two waves read the same x.  Each step
+// issues its x loads before its weight loads: waiting for a stage's x then
+// leaves the younger weight stages in flight (loads complete in order).
+// Workgroup id = ((btile * up_splits) + split) * nblocks + nblock.
+constexpr int kUpKc = 256;                  // k per stage
+constexpr int kUpRowB = kUpKc * 2;          // bytes of one weight row per stage
+constexpr int kUpLoads = 64 * kUpRowB / 16 / 256;  // 16-byte weight pieces per thread per stage
+constexpr int kUpX = kUpKc / 32;            // x pieces (MFMA K steps) per lane per stage
+
+struct UpW {
+  uint4 v[kUpLoads];
+};
+struct UpX {
+  uint4 v[kUpX];
+};
+
 template <int DT>
-__global__ __launch_bounds__(256) void sha_mlp_up_kernel(MlpArgs a) {
+__global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
+  __shared__ __attribute__((aligned(16))) char wsm_[64 * kUpRowB];
   const int nblocks = a.n_pad / 64;
-  int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int t = blockIdx.x;
   const int nblk = t % nblocks;
   t /= nblocks;
   const int split = t % a.up_splits;
   const int btile = t / a.up_splits;
-  if (btile >= a.b_pad / 64) return;          // padding waves of the last workgroup
   const int n_sel = sel_count(a);
   const int n0 = nblk * 64;
-  if (n0 >= n_sel) return;
+  if (n0 >= n_sel) return;                    // whole workgroup: past the selection
   const int b0 = btile * 64;
   const int kbeg = split * a.up_kper;
   const int kend = min(kbeg + a.up_kper, a.d);
+  const int nst = kend > kbeg ? (kend - kbeg) / kUpKc : 0;
 
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c = lane & 15;
-  const char* wrow[4];
-  const char* xrow[4];
-  bool xok[4];
+  lds_char_t* const wl = (lds_char_t*)(wsm_);
+
+  // Weight pieces of this thread: piece index p = tid + 256 i -> row p >> 5
+  // (= (tid >> 5) + 8 i), 16-byte column p & 31; 32-bit byte offsets of the
+  // rows (one weight matrix is below 4 GiB, checked on the host) and the LDS
+  // slot of each piece.
+  const char* w1 = static_cast<const char*>(a.w1t) + static_cast<size_t>(kbeg) * 2;
+  uint32_t woff[kUpLoads];
+  int wdst[kUpLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = sel_row(a, min(n0 + 16 * i + c, n_sel - 1));
-    wrow[i] = static_cast<const char*>(a.w1t) + (static_cast<size_t>(row) * a.d + 8 * q4) * 2;
-    const int b = b0 + 16 * i + c;
-    xok[i] = b < a.B;
-    xrow[i] = static_cast<const char*>(a.x) + (static_cast<size_t>(xok[i] ? b : 0) * a.d + 8 * q4) * 2;
+  for (int i = 0; i < kUpLoads; ++i) {
+    const int r = (tid >> 5) + 8 * i, col = tid & 31;
+    const int row = sel_row(a, min(n0 + r, n_sel - 1));
+    woff[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) * 2u + col * 16;
+    wdst[i] = r * kUpRowB + ((col ^ (r & 15)) * 16);
   }
+  // x row of this lane (padding rows past B read row B - 1 and use zeros).
+  const int b = b0 + 16 * wave + c;
+  const bool xok = b < a.B;
+  const char* xsrc = static_cast<const char*>(a.x) +
+                     (static_cast<size_t>(xok ? b : a.B - 1) * a.d + kbeg + 8 * q4) * 2;
 
-  f32x4 acc[4][4];  // [neuron block][batch block]
+  f32x4 acc[4];  // [neuron block]; batch block = wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = kbeg; k < kend; k += 32 * kUpSteps) {
-    uint4 wv[kUpSteps][4], xv[kUpSteps][4];
+  auto load_w = [&](int st, UpW& d) {
 #pragma unroll
-    for (int u = 0; u < kUpSteps; ++u)
+    for (int i = 0; i < kUpLoads; ++i) d.v[i] = ld16_stream(w1 + woff[i] + st * kUpRowB);
+  };
+  auto load_x = [&](int st, UpX& d) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[u][i] = ld16_stream(wrow[i] + (k + 32 * u) * 2);
+    for (int s = 0; s < kUpX; ++s) d.v[s] = ld16(xsrc + st * kUpRowB + s * 64);
+  };
+  const uint32_t xmask = xok ? 0xFFFFFFFFu : 0u;
+  // Stage st: x of st + 1 and weights of st + 2 go out (CHECK: only those
+  // inside the K range), then stage st goes through LDS into the MFMAs.
+  auto step = [&](int st, UpW& wcur, UpW& wahead, UpX& xcur, UpX& xnext, auto check) {
+    if (!decltype(check)::value || st + 1 < nst) load_x(st + 1, xnext);
+    if (!decltype(check)::value || st + 2 < nst) load_w(st + 2, wahead);
+    __syncthreads();  // the previous stage's LDS reads are done
 #pragma unroll
-    for (int u = 0; u < kUpSteps; ++u)
+    for (int i = 0; i < kUpLoads; ++i)
+      *(lds_u32x4_t*)(wl + wdst[i]) = __builtin_bit_cast(u32x4_t, wcur.v[i]);
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xv[u][i] = xok[i] ? ld16(xrow[i] + (k + 32 * u) * 2) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < kUpX; ++s) {
+      const uint4 xv = xcur.v[s];
+      const uint4 xb = make_uint4(xv.x & xmask, xv.y & xmask, xv.z & xmask, xv.w & xmask);
+      const int piece = 4 * s + q4;         // 16-byte piece of the row this lane reads
 #pragma unroll
-    for (int u = 0; u < kUpSteps; ++u)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = M::mma(wv[u][mb], xv[u][nb], acc[mb][nb]);
+      for (int mb = 0; mb < 4; ++mb) {
+        const u32x4_t av = *(const lds_u32x4_t*)(wl + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
+        acc[mb] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[mb]);
+      }
+    }
+  };
+
+  UpW w0, w1s, w2;
+  UpX x0, x1;
+  if (nst > 0) {
+    load_x(0, x0);
+    load_w(0, w0);
   }
+  if (nst > 1) load_w(1, w1s);
+  // Weights rotate over three sets, x over two: six steps per pass.  Passes
+  // whose look-ahead loads all lie inside the K range run without checks.
+  using Chk = std::true_type;
+  using NoChk = std::false_type;
+  int st = 0;
+  for (; st + 8 <= nst; st += 6) {
+    step(st, w0, w2, x0, x1, NoChk{});
+    step(st + 1, w1s, w0, x1, x0, NoChk{});
+    step(st + 2, w2, w1s, x0, x1, NoChk{});
+    step(st + 3, w0, w2, x1, x0, NoChk{});
+    step(st + 4, w1s, w0, x0, x1, NoChk{});
+    step(st + 5, w2, w1s, x1, x0, NoChk{});
+  }
+  // At most 7 stages remain; the rotation continues where the pass stopped.
+  if (st < nst) step(st, w0, w2, x0, x1, Chk{});
+  if (st + 1 < nst) step(st + 1, w1s, w0, x1, x0, Chk{});
+  if (st + 2 < nst) step(st + 2, w2, w1s, x0, x1, Chk{});
+  if (st + 3 < nst) step(st + 3, w0, w2, x1, x0, Chk{});
+  if (st + 4 < nst) step(st + 4, w1s, w0, x0, x1, Chk{});
+  if (st + 5 < nst) step(st + 5, w2, w1s, x1, x0, Chk{});
+  if (st + 6 < nst) step(st + 6, w0, w2, x0, x1, Chk{});
 
-  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b = b0 + 16 nb + c]
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad: padded rows get zeros)
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int nbase = n0 + 16 * mb + 4 * q4;
     // Entries outside [0, D) (and past the count) produce no activation.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (!sel_valid(a, nbase + r, n_sel)) {
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb][r] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int b = b0 + 16 * nb + c;
-      if (a.up_splits == 1) {
-        const uint32_t lo = M::pack(fmaxf(acc[mb][nb][0], 0.f), fmaxf(acc[mb][nb][1], 0.f));
-        const uint32_t hi = M::pack(fmaxf(acc[mb][nb][2], 0.f), fmaxf(acc[mb][nb][3], 0.f));
-        *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
-                                  (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
-      } else {
-        float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
-        *reinterpret_cast<float4*>(p) =
-            make_float4(acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]);
-      }
+    for (int r = 0; r < 4; ++r)
+      if (!sel_valid(a, nbase + r, n_sel)) acc[mb][r] = 0.f;
+    if (a.up_splits == 1) {
+      const uint32_t lo = M::pack(fmaxf(acc[mb][0], 0.f), fmaxf(acc[mb][1], 0.f));
+      const uint32_t hi = M::pack(fmaxf(acc[mb][2], 0.f), fmaxf(acc[mb][3], 0.f));
+      *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
+                                (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
+    } else {
+      float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
+      *reinterpret_cast<float4*>(p) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
     }
   }
 }
@@ -423,25 +518,33 @@ __global__ __launch_bounds__(256) void sha_mlp_down_kernel(MlpArgs a) {
     }
 }
 
-// y = sum of the neuron-split partials, fixed order.
+// y = sum of the neuron-split partials, fixed order; one thread per 4
+// consecutive columns (d is a multiple of 256).
 template <int DT>
 __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
-  const size_t total = static_cast<size_t>(a.B) * a.d;
-  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += static_cast<size_t>(gridDim.x) * 256) {
-    const size_t b = i / a.d, col = i % a.d;
-    float s = 0.f;
-    for (int sp = 0; sp < a.dn_splits; ++sp)
-      s += a.dn_part[(static_cast<size_t>(sp) * a.b_pad + b) * a.d + col];
-    Elem<DT>::store(a.y, i, s);
+  const size_t quads = static_cast<size_t>(a.B) * (a.d / 4);
+  const size_t plane = static_cast<size_t>(a.b_pad) * a.d;
+  for (size_t i = blockIdx.x * 256 + threadIdx.x; i < quads; i += static_cast<size_t>(gridDim.x) * 256) {
+    const float4* p = reinterpret_cast<const float4*>(a.dn_part) + i;  // row-major [b][d] of plane 0
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < a.dn_splits; ++sp) {
+      const float4 v = p[sp * (plane / 4)];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const size_t e = i * 4;
+    Elem<DT>::store(a.y, e, s.x);
+    Elem<DT>::store(a.y, e + 1, s.y);
+    Elem<DT>::store(a.y, e + 2, s.z);
+    Elem<DT>::store(a.y, e + 3, s.w);
   }
 }
 
 template <int DT>
 hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
-  const long long up_waves = static_cast<long long>(a.n_pad / 64) * a.up_splits * btiles;
-  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(static_cast<unsigned>((up_waves + 3) / 4)),
-                     dim3(256), 0, st, a);
+  const long long up_wgs = static_cast<long long>(a.n_pad / 64) * a.up_splits * btiles;
+  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
+                     st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.up_splits > 1) {
@@ -454,8 +557,8 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dn_splits > 1) {
-    const size_t total = static_cast<size_t>(a.B) * a.d;
-    const unsigned blocks = static_cast<unsigned>(total < 256 * 1024 ? (total + 255) / 256 : 1024);
+    const size_t total = static_cast<size_t>(a.B) * (a.d / 4);
+    const unsigned blocks = static_cast<unsigned>(total < 256 * 2048 ? (total + 255) / 256 : 2048);
     hipLaunchKernelGGL((sha_mlp_down_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
@@ -464,8 +567,10 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int mlp_union_blocks(int D) { return (D + kUnionBlockFlags - 1) / kUnionBlockFlags; }
+
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, hipStream_t st) {
+                            uint8_t* flags, int32_t* counts, hipStream_t st) {
   const int n16 = (D + 15) / 16;
   hipLaunchKernelGGL(sha_mlp_union_clear_kernel, dim3(min((n16 + 255) / 256, 1024)), dim3(256), 0,
                      st, flags, D);
@@ -476,8 +581,12 @@ hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel,
                        0, st, rows, total, D, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(sha_mlp_union_compact_kernel, dim3(1), dim3(kUnionThreads), 0, st, flags, D,
-                     sel, n_sel);
+  const int nb = mlp_union_blocks(D);
+  hipLaunchKernelGGL(sha_mlp_union_count_kernel, dim3(nb), dim3(kUnionBlockThreads), 0, st, flags,
+                     D, counts);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(sha_mlp_union_write_kernel, dim3(nb), dim3(kUnionBlockThreads), 0, st, flags,
+                     D, counts, sel, n_sel);
   return hipGetLastError();
 }
 

@@ -138,7 +138,8 @@ def test_mlp_host_validation():
     assert L.sha_mlp_union(P, 2, 3, 10, None, P, None, P, big) == 1
     assert L.sha_mlp_union(None, 2, 3, 10, P, P, None, P, big) == 1
     assert L.sha_mlp_union(P + 2, 2, 3, 10, P, P, None, P, big) == 3
-    assert L.sha_mlp_union_workspace_bytes(1000) == 1024
+    assert L.sha_mlp_union_workspace_bytes(1000) == 1024 + 256     # flags, block counts
+    assert L.sha_mlp_union_workspace_bytes(36864) == 36864 + 256
     assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, P, 1023) == 4
     assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, None, big) == 4
 
@@ -161,15 +162,19 @@ def test_mlp_host_validation():
 def test_mlp_workspace_accounting():
     L = bd.lib()
     # OPT-66B MLP, all 36864 neurons selected, 64 rows, 256 CUs: H (64 x 36864
-    # 16-bit), the up projection's fp32 partials over 3 K splits (576 waves x 3
-    # fill 8 waves per CU once) and the down projection's over 14 neuron
-    # splits (36 column blocks x 14 ~ 2 workgroups per CU).
+    # 16-bit), the up projection's fp32 partials over 3 K splits (576
+    # workgroups exceed the 512 resident slots; 3 splits give 4 rounds of
+    # 1/3-size work) and the down projection's over 14 neuron splits (36
+    # column blocks x 14 ~ 2 workgroups per CU).
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 36864, 256)
     assert ws == 64 * 36864 * 2 + 3 * 64 * 36864 * 4 + 14 * 64 * 9216 * 4
-    # a 64-neuron selection splits the up projection's K 15 ways (16 wanted,
-    # 640-element ranges) and keeps a single down split
+    # 21056 padded neurons (329 workgroups: half to all of the slots): no split
+    ws = L.sha_selective_mlp_workspace_bytes(8, 9216, 36864, 21033, 256)
+    assert ws == 64 * 21056 * 2 + 14 * 64 * 9216 * 4
+    # a 64-neuron selection splits the up projection's K 8 ways (1280-element
+    # ranges: 8 splits) and keeps a single down split
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
-    assert ws == 64 * 64 * 2 + 15 * 64 * 64 * 4
+    assert ws == 64 * 64 * 2 + 8 * 64 * 64 * 4
 
 
 def test_router_host_validation():

@@ -35,7 +35,8 @@ def _run(x, w1t, w2t, sel, n_sel, n_max=None):
 
 
 @pytest.mark.parametrize("B,k,D", [(1, 5, 100), (7, 40, 1000), (64, 300, 5000), (3, 0, 10),
-                                   (5, 33, 40000)])
+                                   (5, 33, 40000), (9, 500, 100000), (64, 3686, 36864),
+                                   (2, 70000, 65537)])
 def test_union_matches_oracle(B, k, D):
     say(f"[mlp] union B={B} k={k} D={D}")
     rng = np.random.default_rng(B * 1000 + k)
