@@ -61,6 +61,7 @@ def parse():
                    help="rotating K/V copies (0 = enough that consecutive steps share no bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calib", action="store_true")
     p.add_argument("--summarize-traffic", action="store_true",
@@ -117,6 +118,34 @@ def time_calls(call, steps: int, warmup: int, stream):
     return wall / steps * 1e3, ev_ms
 
 
+def read_probe(dev, nbytes: int = 1 << 31):
+    """Secondary ceiling: the best streaming-read rate of libsha_probe.so (the
+    head kernel's access pattern: 1 KiB non-temporal wave loads, 8 in flight)
+    over a few grid sizes, on a buffer far larger than the caches."""
+    import ctypes
+    path = os.path.join(ROOT, "contextual_head_sparsity_amd", "libsha_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.sha_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    buf = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = (0.0, 0)
+    for blocks in (1024, 2048, 4096, 8192):
+        def call(i):
+            st = L.sha_probe_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"sha_probe_read failed: {st}")
+        _, ev = time_calls(call, 10, 3, stream)
+        gbs = nbytes / (float(np.median(ev)) / 1e3) / 1e9
+        best = max(best, (gbs, blocks))
+    del buf
+    return {"GBps": round(best[0], 1), "blocks": best[1], "bytes": nbytes,
+            "kernel": "sha_probe_read_kernel (libsha_probe.so)"}
+
+
 def cpu_baseline(w, q, k, v, idx, budget_s: float):
     """The fp64 oracle on the host cores: whole layer calls of this workload
     (every active unit, inputs copied to host memory first), repeated until
@@ -145,8 +174,14 @@ def cpu_baseline(w, q, k, v, idx, budget_s: float):
         spent += time.perf_counter() - t0
         passes += 1
     per_call = spent / passes
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
     return {"value": round(w.active_kv_bytes / per_call / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
+            "us_per_layer": round(per_call * 1e6, 1), "os_cpu_count": os.cpu_count(),
+            "affinity_cores": affinity, "blas_threads": threads,
             "sample": f"{passes} full layer call(s) of {w.name} ({w.units} units, "
                       f"{w.active_kv_bytes / 1e6:.0f} MB active K/V each), fp64 numpy oracle, "
                       f"{spent:.1f} s timed, {per_call * 1e6:.0f} us per layer call"}
@@ -467,6 +502,7 @@ def main():
                      "traffic": traffic,
                      "kernel": "sha_decode_gqa_mfma_kernel" if w.gqa else "sha_decode_mha_kernel",
                      "launch_avg_us": round(ev_avg_ms * 1e3, 2),
+                     "launch_median_us": round(float(np.median(ev)) * 1e3, 2),
                      "launch_p10_us": round(float(np.percentile(ev, 10)) * 1e3, 2),
                      "launch_p90_us": round(float(np.percentile(ev, 90)) * 1e3, 2),
                      "bytes_per_launch": w.active_kv_bytes,
@@ -474,6 +510,9 @@ def main():
                               if nsplit > 1 else "event span covers the one decode kernel")},
         "all_heads": dense,
     }
+    probe = read_probe(dev) if not args.no_probe else None
+    out["read_probe"] = probe
+    out["pct_of_read_probe"] = round(100 * value / probe["GBps"], 2) if probe else None
     if not args.no_cpu_baseline and layout == "contig":
         out["cpu_baseline"] = cpu_baseline(w, q, ks[0], vs[0], idx, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsha.so")
+PROBE_LIB = os.path.join(PKG, "libsha_probe.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are disabled for all device code; hipcc's host pass
@@ -55,6 +56,11 @@ def build(verbose: bool = True) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    # The benchmark's read-bandwidth probe: a library of its own.
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
+          os.path.join(PKG, "probe", "sha_probe.hip"), "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -276,3 +276,19 @@ def test_step_host_validation():
     assert L.sha_step_create(None, None, 1, 1, ctypes.byref(h)) == 1
     assert L.sha_step_run(None, None) == 1
     assert L.sha_step_destroy(None) == 1
+
+
+def test_read_probe_library():
+    """The benchmark's read-bandwidth probe loads and rejects bad arguments
+    before launching anything."""
+    path = os.path.join(os.path.dirname(bd.LIB_PATH), "libsha_probe.so")
+    assert os.path.exists(path)
+    P = ctypes.CDLL(path)
+    P.sha_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    EINVAL = -1
+    assert P.sha_probe_read(None, 1 << 20, 4, A16, None) == EINVAL
+    assert P.sha_probe_read(A16, 1 << 20, 4, None, None) == EINVAL
+    assert P.sha_probe_read(A16, 1 << 20, 0, A16, None) == EINVAL
+    assert P.sha_probe_read(A16, (1 << 20) + 16, 4, A16, None) == EINVAL   # not whole 32 KiB steps
+    assert P.sha_probe_read(A16 + 8, 1 << 20, 4, A16, None) == EINVAL      # misaligned
