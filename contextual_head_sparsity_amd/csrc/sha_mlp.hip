@@ -391,8 +391,10 @@ constexpr int kDnCols = 256;                // output columns per workgroup
 constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 B: conflict-free transposed reads
 constexpr int kDnHPitch = kDnKc * 2 + 16;   // 144 B: conflict-free H reads
 
+// Two workgroups per CU (the planner's assumption): the register budget is
+// held at 256 per lane, accumulators included.
 template <int DT>
-__global__ __launch_bounds__(256) void sha_mlp_down_kernel(MlpArgs a) {
+__global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   using M = Mx<DT>;
   __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
   __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
