@@ -213,14 +213,17 @@ __device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
 // A workgroup owns 64 selected neurons x 64 batch rows over a K range, in
 // stages of kUpKc = 256 k.  Each stage's weights (64 rows x 512 B) are read
 // with 128-bit non-temporal loads, two rows of 512 contiguous bytes per wave
-// instruction, two stages ahead (three register sets in rotation), and
-// written to LDS with an XOR swizzle of the 16-byte pieces
-// (slot = piece ^ (row & 15)), so that the A-operand reads (16 rows x one
-// piece per quarter wave) hit distinct banks.  Wave w multiplies all 64
-// neurons by batch block w: its x pieces (B operands) come from L2 into
-// registers one stage ahead, and no two waves read the same x.  Each step
-// issues its x loads before its weight loads: waiting for a stage's x then
-// leaves the younger weight stages in flight (loads complete in order).
+// instruction, three stages ahead of their use (two register sets: a set is
+// reloaded as soon as it is written to LDS), and written one stage ahead
+// into a double-buffered LDS tile with an XOR
+// swizzle of the 16-byte pieces (slot = piece ^ (row & 15)), so that the
+// A-operand reads (16 rows x one piece per quarter wave) hit distinct banks;
+// one barrier per stage both publishes the next tile and retires the one
+// just read.  Wave w multiplies all 64 neurons by batch block w: its x pieces
+// (B operands) come from L2 into registers one stage ahead, and no two waves
+// read the same x.  Each step issues its x loads before its weight loads:
+// waiting for a stage's x then leaves the younger weight stages in flight
+// (loads complete in order).
 // Workgroup id = ((btile * up_splits) + split) * nblocks + nblock.
 constexpr int kUpKc = 256;                  // k per stage
 constexpr int kUpRowB = kUpKc * 2;          // bytes of one weight row per stage
@@ -237,7 +240,7 @@ struct UpX {
 template <int DT>
 __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
-  __shared__ __attribute__((aligned(16))) char wsm_[64 * kUpRowB];
+  __shared__ __attribute__((aligned(16))) char wsm_[2 * 64 * kUpRowB];
   const int nblocks = a.n_pad / 64;
   int t = blockIdx.x;
   const int nblk = t % nblocks;
@@ -289,16 +292,23 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     for (int s = 0; s < kUpX; ++s) d.v[s] = ld16(xsrc + st * kUpRowB + s * 64);
   };
   const uint32_t xmask = xok ? 0xFFFFFFFFu : 0u;
-  // Stage st: x of st + 1 and weights of st + 2 go out (CHECK: only those
-  // inside the K range), then stage st goes through LDS into the MFMAs.
-  auto step = [&](int st, UpW& wcur, UpW& wahead, UpX& xcur, UpX& xnext, auto check) {
-    if (!decltype(check)::value || st + 1 < nst) load_x(st + 1, xnext);
-    if (!decltype(check)::value || st + 2 < nst) load_w(st + 2, wahead);
-    __syncthreads();  // the previous stage's LDS reads are done
+  auto write_w = [&](int st, const UpW& w) {
+    lds_char_t* const buf = wl + (st & 1) * (64 * kUpRowB);
 #pragma unroll
     for (int i = 0; i < kUpLoads; ++i)
-      *(lds_u32x4_t*)(wl + wdst[i]) = __builtin_bit_cast(u32x4_t, wcur.v[i]);
-    __syncthreads();
+      *(lds_u32x4_t*)(buf + wdst[i]) = __builtin_bit_cast(u32x4_t, w.v[i]);
+  };
+  // Step st: the weights of st + 1 go from registers to LDS, which frees
+  // their register set for the weights of st + 3; x of st + 1 goes out
+  // first; stage st is multiplied; one barrier closes the step (CHECK: only
+  // work inside the K range).  Weights of stage j live in set j % 2, x of
+  // stage j in x set j % 2.
+  auto step = [&](int st, UpW& wnext, UpX& xcur, UpX& xnext, auto check) {
+    constexpr bool C = decltype(check)::value;
+    if (!C || st + 1 < nst) write_w(st + 1, wnext);
+    if (!C || st + 1 < nst) load_x(st + 1, xnext);
+    if (!C || st + 3 < nst) load_w(st + 3, wnext);
+    const lds_char_t* const buf = wl + (st & 1) * (64 * kUpRowB);
 #pragma unroll
     for (int s = 0; s < kUpX; ++s) {
       const uint4 xv = xcur.v[s];
@@ -306,40 +316,37 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
       const int piece = 4 * s + q4;         // 16-byte piece of the row this lane reads
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const u32x4_t av = *(const lds_u32x4_t*)(wl + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
+        const u32x4_t av = *(const lds_u32x4_t*)(buf + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
         acc[mb] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[mb]);
       }
     }
+    __syncthreads();
   };
 
-  UpW w0, w1s, w2;
+  UpW wa, wb;
   UpX x0, x1;
   if (nst > 0) {
     load_x(0, x0);
-    load_w(0, w0);
+    load_w(0, wa);
   }
-  if (nst > 1) load_w(1, w1s);
-  // Weights rotate over three sets, x over two: six steps per pass.  Passes
-  // whose look-ahead loads all lie inside the K range run without checks.
+  if (nst > 1) load_w(1, wb);
+  if (nst > 0) write_w(0, wa);
+  if (nst > 2) load_w(2, wa);
+  __syncthreads();
+  // Two steps per pass; passes whose look-ahead work all lies inside the K
+  // range run without checks.
   using Chk = std::true_type;
   using NoChk = std::false_type;
   int st = 0;
-  for (; st + 8 <= nst; st += 6) {
-    step(st, w0, w2, x0, x1, NoChk{});
-    step(st + 1, w1s, w0, x1, x0, NoChk{});
-    step(st + 2, w2, w1s, x0, x1, NoChk{});
-    step(st + 3, w0, w2, x1, x0, NoChk{});
-    step(st + 4, w1s, w0, x0, x1, NoChk{});
-    step(st + 5, w2, w1s, x1, x0, NoChk{});
+  for (; st + 5 <= nst; st += 2) {
+    step(st, wb, x0, x1, NoChk{});
+    step(st + 1, wa, x1, x0, NoChk{});
   }
-  // At most 7 stages remain; the rotation continues where the pass stopped.
-  if (st < nst) step(st, w0, w2, x0, x1, Chk{});
-  if (st + 1 < nst) step(st + 1, w1s, w0, x1, x0, Chk{});
-  if (st + 2 < nst) step(st + 2, w2, w1s, x0, x1, Chk{});
-  if (st + 3 < nst) step(st + 3, w0, w2, x1, x0, Chk{});
-  if (st + 4 < nst) step(st + 4, w1s, w0, x0, x1, Chk{});
-  if (st + 5 < nst) step(st + 5, w2, w1s, x1, x0, Chk{});
-  if (st + 6 < nst) step(st + 6, w0, w2, x0, x1, Chk{});
+  for (; st + 2 <= nst; st += 2) {
+    step(st, wb, x0, x1, Chk{});
+    step(st + 1, wa, x1, x0, Chk{});
+  }
+  if (st < nst) step(st, wb, x0, x1, Chk{});
 
   // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad: padded rows get zeros)
 #pragma unroll
