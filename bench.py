@@ -121,7 +121,8 @@ def time_calls(call, steps: int, warmup: int, stream):
 def read_probe(dev, nbytes: int = 1 << 31):
     """Secondary ceiling: the best streaming-read rate of libsha_probe.so (the
     head kernel's access pattern: 1 KiB non-temporal wave loads, 8 in flight)
-    over a few grid sizes, on a buffer far larger than the caches."""
+    over grid sizes from one to sixteen workgroups per CU, on a buffer far
+    larger than the caches."""
     import ctypes
     path = os.path.join(ROOT, "contextual_head_sparsity_amd", "libsha_probe.so")
     if not os.path.exists(path):
@@ -133,7 +134,7 @@ def read_probe(dev, nbytes: int = 1 << 31):
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     best = (0.0, 0)
-    for blocks in (1024, 2048, 4096, 8192):
+    for blocks in (256, 512, 1024, 2048, 4096):
         def call(i):
             st = L.sha_probe_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), stream.cuda_stream)
             if st != 0:
