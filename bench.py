@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--write-csv")
     p.add_argument("--copy-fetch-csv")
     p.add_argument("--copy-write-csv")
+    p.add_argument("--traffic-out", default=None,
+                   help="where --summarize-traffic writes (default: profiles/traffic_<workload>.json)")
     p.add_argument("--grid", type=int, default=0, help="decode dispatch grid size to select")
     p.add_argument("--mlp", default=None, choices=list(wl.MLP_WORKLOADS),
                    help="measure the selective MLP on this workload instead of SHA decode")
@@ -246,7 +248,7 @@ def summarize_traffic(args):
            "hbm_bytes_per_launch": read_b + write_b,
            "algorithmic_bytes_per_launch": w.active_kv_bytes,
            "ratio_to_algorithmic": (read_b + write_b) / w.active_kv_bytes}
-    with open(traffic_path(w.name), "w") as f:
+    with open(args.traffic_out or traffic_path(w.name), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
@@ -400,8 +402,9 @@ def main():
         summarize_traffic(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: SHA decode units are independent and this "
-              "build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
+        print("bench.py measures one GPU: SHA decode units are independent and the "
+              "library runs each layer call on a single MI355X; --gpus must be 1.",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
