@@ -292,3 +292,17 @@ def test_read_probe_library():
     assert P.sha_probe_read(A16, 1 << 20, 0, A16, None) == EINVAL
     assert P.sha_probe_read(A16, (1 << 20) + 16, 4, A16, None) == EINVAL   # not whole 32 KiB steps
     assert P.sha_probe_read(A16 + 8, 1 << 20, 4, A16, None) == EINVAL      # misaligned
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without libsha.so every entry point raises."""
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "libsha.so"))
+    monkeypatch.setattr(bd, "_lib", None)
+    with pytest.raises(ImportError):
+        bd.lib()
+    with pytest.raises(ImportError):
+        bd.plan_nsplit(1, 4, 4, 64, 64, 1)
+    with pytest.raises(ImportError):
+        bd.workspace_bytes(1, 4, 4, 64, 64, 1)
+    with pytest.raises(ImportError):
+        bd.selective_mlp_workspace_bytes(1, 256, 512, 64)
