@@ -115,9 +115,9 @@ int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int 
   return static_cast<int>(ns);
 }
 
-// Effective split geometry: `chunk` keys per split (a multiple of 16 keys,
-// and of the page size for a paged cache, when there is more than one
-// split), every split non-empty.  A paged cache (page > 0) also keeps every
+// Effective split geometry: `chunk` keys per split (when there is more than
+// one split: a multiple of 16 keys, of 128 keys for splits of 512 keys or
+// more, and of the page size for a paged cache), every split non-empty.  A paged cache (page > 0) also keeps every
 // split within sha::kMaxSplitPages pages, the page ids a workgroup stages.
 void split_geometry(int Nkv, int nsplit_req, int page, int* nsplit, int* chunk) {
   int ns = nsplit_req < 1 ? 1 : (nsplit_req > Nkv ? Nkv : nsplit_req);
@@ -131,8 +131,12 @@ void split_geometry(int Nkv, int nsplit_req, int page, int* nsplit, int* chunk) 
     *chunk = Nkv;
     return;
   }
-  const int align = page > 16 ? page : 16;
   int c = (Nkv + ns - 1) / ns;
+  // Splits of 512 keys or more end on a whole kernel iteration (128 keys:
+  // 4 waves x 4 rows x 8 for the head kernel, 4 waves x 32-key tiles for the
+  // group kernel), so that only the last split has a ragged tail.
+  int align = c >= 512 ? 128 : 16;
+  if (page > align) align = page;
   c = (c + align - 1) / align * align;
   *chunk = c;
   *nsplit = (Nkv + c - 1) / c;
