@@ -9,13 +9,16 @@
 // (batch_head_index [B, top_k], ascending), so router -> attention needs no
 // host synchronisation.
 //
-//   scores kernel: one wave per (batch row, 8 consecutive heads); lanes split
-//                  the hidden dimension in 16-byte pieces (v_dot2 for 16-bit
-//                  inputs, fp32 accumulation), DPP + shuffle wave sums.
-//   top-k kernel : one wave per batch row; k rounds of a wave-wide argmax
-//                  (ties to the lower head index, NaN ranked as -inf), then
-//                  the picked heads are written in ascending order with a
-//                  ballot prefix count.
+//   scores kernel: one workgroup per (batch row, 8 consecutive heads); its
+//                  four waves take a quarter of the hidden dimension each in
+//                  16-byte pieces (v_dot2 for 16-bit inputs, fp32
+//                  accumulation), DPP + shuffle wave sums, the quarters
+//                  added in a fixed order.
+//   top-k kernel : one wave per batch row; each head's rank in the (score
+//                  descending, index ascending) order is counted against the
+//                  row staged in LDS (NaN ranked as -inf) and the heads of
+//                  rank < k are written in ascending order with a ballot
+//                  prefix count.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,102 +37,154 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int kScoreHeads = 8;   // heads per scores workgroup
+constexpr int kScoreWaves = 4;   // the hidden dimension is cut in 4 contiguous quarters
+constexpr int kScoreUnroll = 4;  // 16-byte pieces per lane in flight per head (and of x)
+
+// One workgroup per (batch row, 8 consecutive heads); wave w dots the w-th
+// quarter of the hidden dimension, kScoreUnroll pieces of x and of each head's
+// row in flight per lane; the four quarters are added in a fixed order.
 template <int DT>
-__global__ __launch_bounds__(256) void sha_router_scores_kernel(RouterArgs a) {
+__global__ __launch_bounds__(kScoreWaves * 64) void sha_router_scores_kernel(RouterArgs a) {
   using E = Elem<DT>;
   constexpr int VEC = E::VEC;
   constexpr int ES = 16 / VEC;
-  const int nhg = (a.H + 7) / 8;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = wid / nhg, hg = wid % nhg;
-  if (b >= a.B) return;
-  const int lane = threadIdx.x & 63;
+  __shared__ float part[kScoreWaves][kScoreHeads];
+  const int nhg = (a.H + kScoreHeads - 1) / kScoreHeads;
+  const int b = blockIdx.x / nhg, hg = blockIdx.x % nhg;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Quarter of the hidden dimension, in whole 16-byte pieces.
+  const int pieces = a.d / VEC;
+  const int q0 = (pieces * wave) / kScoreWaves, q1 = (pieces * (wave + 1)) / kScoreWaves;
   const char* xr = static_cast<const char*>(a.x) + static_cast<size_t>(b) * a.d * ES;
   const char* wb = static_cast<const char*>(a.w);
-  float acc[8];
+  float acc[kScoreHeads];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int k = lane * VEC; k < a.d; k += 64 * VEC) {
-    const uint4 xv = ld16(xr + k * ES);
+  for (int j = 0; j < kScoreHeads; ++j) acc[j] = 0.f;
+  // Loads are unconditional (clamped to the quarter's last piece and to head
+  // H - 1) so that all of them are in flight together; pieces past the
+  // quarter add nothing and heads past H are never stored.
+  for (int p0 = q0 + lane; p0 < q1; p0 += 64 * kScoreUnroll) {
+    uint4 xv[kScoreUnroll], wv[kScoreUnroll][kScoreHeads];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int h = hg * 8 + j;
-      if (h < a.H) acc[j] += E::dot(xv, ld16(wb + (static_cast<size_t>(h) * a.d + k) * ES));
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int p = min(p0 + 64 * u, q1 - 1);
+      xv[u] = ld16(xr + static_cast<size_t>(p) * 16);
+#pragma unroll
+      for (int j = 0; j < kScoreHeads; ++j) {
+        const int h = min(hg * kScoreHeads + j, a.H - 1);
+        wv[u][j] = ld16(wb + (static_cast<size_t>(h) * a.d * ES) + static_cast<size_t>(p) * 16);
+      }
+    }
+    // Keep every load above the first use: the scheduler would otherwise
+    // interleave them with the dot products and wait on each in turn.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const bool ok = p0 + 64 * u < q1;
+#pragma unroll
+      for (int j = 0; j < kScoreHeads; ++j) {
+        const float t = E::dot(xv[u], wv[u][j]);
+        acc[j] += ok ? t : 0.f;
+      }
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kScoreHeads; ++j) {
     const float s = wave_sum(acc[j]);
-    const int h = hg * 8 + j;
-    if (lane == j && h < a.H)
+    if (lane == 0) part[wave][j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < kScoreHeads) {
+    const int j = threadIdx.x, h = hg * kScoreHeads + j;
+    if (h < a.H) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kScoreWaves; ++w) s += part[w][j];
       a.scores[static_cast<size_t>(b) * a.H + h] = s + (a.bias ? a.bias[h] : 0.f);
+    }
   }
 }
-
-constexpr int kRouterSlots = kRouterMaxH / 64;   // scores per lane
 
 // (value, index) ordering of the top-k: larger value first, then lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// One wave per batch row.  Head h is picked when fewer than top_k heads rank
+// before it in the (score descending, index ascending) order, NaN ranked as
+// -inf: every lane counts, for its heads, how many of the row's H scores
+// (staged in LDS, read as broadcasts) come first.  The picked heads are then
+// written in ascending order with a ballot prefix count.  SLOTS = heads per
+// lane (H <= 64 SLOTS), a compile-time count so that the counting loop has
+// no branches.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void sha_router_topk_kernel(RouterArgs a) {
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) float row_sc[4][64 * SLOTS];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + wave;
   if (b >= a.B) return;
-  const int lane = threadIdx.x & 63;
   const float* srow = a.scores + static_cast<size_t>(b) * a.H;
-  float v[kRouterSlots];
+  float* sc = row_sc[wave];
+  float v[SLOTS];
+  // Unconditional (clamped) loads, all in flight together.
 #pragma unroll
-  for (int i = 0; i < kRouterSlots; ++i) {
+  for (int i = 0; i < SLOTS; ++i) v[i] = srow[min(lane + 64 * i, a.H - 1)];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
     const int h = lane + 64 * i;
-    float x = h < a.H ? srow[h] : kNegInf;
-    v[i] = (x != x) ? kNegInf : x;  // NaN ranks like -inf
+    float x = v[i];
+    x = (h >= a.H || x != x) ? kNegInf : x;  // NaN ranks like -inf
+    v[i] = x;
+    // Entries past H hold -inf: with an index of H or more they never rank
+    // before a real head.
+    sc[h] = x;
   }
-  uint32_t taken = 0;
-  for (int r = 0; r < a.top_k; ++r) {
-    float bv = kNegInf;
-    int bi = 0x7FFFFFFF;
+  __builtin_amdgcn_wave_barrier();
+  int rank[SLOTS];
 #pragma unroll
-    for (int i = 0; i < kRouterSlots; ++i) {
-      const int h = lane + 64 * i;
-      if (!((taken >> i) & 1u) && better(v[i], h, bv, bi)) {
-        bv = v[i];
-        bi = h;
-      }
-    }
+  for (int i = 0; i < SLOTS; ++i) rank[i] = 0;
+  for (int h2 = 0; h2 < a.H; h2 += 4) {
+    const float4 o4 = *reinterpret_cast<const float4*>(sc + h2);
+    const float o[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i)
+        rank[i] += better(o[e], h2 + e, v[i], lane + 64 * i) ? 1 : 0;
   }
-  // Picked heads in ascending order: slot i holds heads 64 i .. 64 i + 63.
   int base = 0;
   int32_t* irow = a.index + static_cast<size_t>(b) * a.top_k;
 #pragma unroll
-  for (int i = 0; i < kRouterSlots; ++i) {
-    const bool mine = (taken >> i) & 1u;
+  for (int i = 0; i < SLOTS; ++i) {
+    const int h = lane + 64 * i;
+    const bool mine = h < a.H && rank[i] < a.top_k;
     const unsigned long long mask = __ballot(mine);
-    if (mine) irow[base + __popcll(mask & ((1ull << lane) - 1ull))] = lane + 64 * i;
+    if (mine) irow[base + __popcll(mask & ((1ull << lane) - 1ull))] = h;
     base += __popcll(mask);
   }
 }
 
+template <int SLOTS>
+hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((sha_router_topk_kernel<SLOTS>), dim3(static_cast<unsigned>((a.B + 3) / 4)),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
-  const long long waves = static_cast<long long>(a.B) * ((a.H + 7) / 8);
-  hipLaunchKernelGGL((sha_router_scores_kernel<DT>), dim3(static_cast<unsigned>((waves + 3) / 4)),
-                     dim3(256), 0, st, a);
+  const long long wgs = static_cast<long long>(a.B) * ((a.H + kScoreHeads - 1) / kScoreHeads);
+  hipLaunchKernelGGL((sha_router_scores_kernel<DT>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(kScoreWaves * 64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.top_k == 0) return e;
-  hipLaunchKernelGGL(sha_router_topk_kernel, dim3(static_cast<unsigned>((a.B + 3) / 4)), dim3(256),
-                     0, st, a);
-  return hipGetLastError();
+  const int slots = (a.H + 63) / 64;
+  if (slots <= 1) return launch_topk<1>(a, st);
+  if (slots <= 2) return launch_topk<2>(a, st);
+  if (slots <= 4) return launch_topk<4>(a, st);
+  if (slots <= 8) return launch_topk<8>(a, st);
+  return launch_topk<kRouterMaxH / 64>(a, st);
 }
 
 }  // namespace
