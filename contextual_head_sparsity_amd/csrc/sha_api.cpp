@@ -538,9 +538,7 @@ size_t sha_workspace_bytes(int B, int H, int H_kv, int Nkv, int d, int top_k, in
 }
 
 size_t sha_mlp_union_workspace_bytes(int D) {
-  if (D < 1) return 0;
-  return round256(static_cast<size_t>(D)) +
-         round256(static_cast<size_t>(sha::mlp_union_blocks(D)) * sizeof(int32_t));
+  return D < 1 ? 0 : round256(static_cast<size_t>(D));
 }
 
 sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_t* sel,
@@ -555,10 +553,8 @@ sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_
   if (!workspace || workspace_bytes < sha_mlp_union_workspace_bytes(D)) return SHA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
   (void)hipGetLastError();
-  uint8_t* flags = static_cast<uint8_t*>(workspace);
-  int32_t* counts = reinterpret_cast<int32_t*>(flags + round256(static_cast<size_t>(D)));
   const hipError_t e = sha::launch_mlp_union(row_neurons, static_cast<int>(total), D, sel, n_sel,
-                                             flags, counts, stream);
+                                             static_cast<uint8_t*>(workspace), stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;
     return SHA_ERR_HIP;

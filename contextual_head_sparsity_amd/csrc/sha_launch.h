@@ -85,11 +85,10 @@ struct MlpArgs {
   int dn_splits;        // neuron-range splits of the down projection
 };
 
-// flags: round_up(D, 256) bytes of workspace; counts: mlp_union_blocks(D)
-// int32 block counts, also workspace.
+// flags: round_up(D, 256) bytes of workspace.
 int mlp_union_blocks(int D);
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, int32_t* counts, hipStream_t stream);
+                            uint8_t* flags, hipStream_t stream);
 hipError_t launch_selective_mlp(const MlpArgs& a, int dtype, hipStream_t stream);
 
 // Attention router: scores = x w^T (+ bias), per-row top-k heads.

@@ -11,10 +11,9 @@
 // Kernels:
 //   union  - a flag byte per neuron in a workspace: cleared, marked by every
 //            row's entries (plain byte stores, any order gives the same flags),
-//            counted per 4096-flag block, then every block writes its marked
-//            neurons in ascending order at the offset the earlier blocks'
-//            counts give, and the last block writes the total (deterministic,
-//            on device).
+//            then every 4096-flag block counts the flags before it (its
+//            output offset), writes its marked neurons in ascending order,
+//            and the last block writes the total (deterministic, on device).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
 //            a workgroup owns 64 selected neurons x 64 batch rows over a K
 //            range; weight rows stream in 512-byte runs (non-temporal
@@ -112,11 +111,11 @@ __global__ __launch_bounds__(256) void sha_mlp_union_mark_kernel(const int32_t* 
   }
 }
 
-// Compaction in two launches over blocks of kUnionBlockFlags flags (one
-// 16-flag word per thread): `count` stores each block's number of set flags;
-// `write` sums the counts of the blocks before its own (its output offset),
-// scans its words, gathers its neurons in LDS in ascending order and copies
-// them out with contiguous stores; the last block also stores the total.
+// Compaction in one launch over blocks of kUnionBlockFlags flags (one
+// 16-flag word per thread): a block counts the set flags of all the blocks
+// before its own (its output offset; at most D bytes, read from L2), scans
+// its words, gathers its neurons in LDS in ascending order and copies them
+// out with contiguous stores; the last block also stores the total.
 constexpr int kUnionBlockFlags = 4096;
 constexpr int kUnionBlockThreads = kUnionBlockFlags / 16;
 
@@ -146,36 +145,26 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_sums, 
   return v + before;
 }
 
-__global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_count_kernel(
-    const uint8_t* flags, int D, int32_t* counts) {
-  __shared__ uint32_t wave_sums[kUnionBlockThreads / 64];
-  const int word = blockIdx.x * kUnionBlockThreads + threadIdx.x;
-  const int n16 = (D + 15) / 16;   // flags past D in the last word are cleared zeros
-  const uint32_t c = word < n16 ? flag_count(reinterpret_cast<const uint4*>(flags)[word]) : 0u;
-  uint32_t total;
-  block_scan(c, wave_sums, &total);
-  if (threadIdx.x == 0) counts[blockIdx.x] = static_cast<int32_t>(total);
-}
-
 __global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_write_kernel(
-    const uint8_t* flags, int D, const int32_t* counts, int32_t* sel, int32_t* n_sel) {
+    const uint8_t* flags, int D, int32_t* sel, int32_t* n_sel) {
   __shared__ uint32_t wave_sums[kUnionBlockThreads / 64];
   __shared__ int32_t staged[kUnionBlockFlags];
   __shared__ uint32_t base_sh;
   const int tid = threadIdx.x;
-  // Output offset of this block: the counts of the blocks before it.
+  const uint4* fw = reinterpret_cast<const uint4*>(flags);
+  // Output offset of this block: the set flags of the blocks before it.
   uint32_t part = 0;
-  for (int q = tid; q < static_cast<int>(blockIdx.x); q += kUnionBlockThreads)
-    part += static_cast<uint32_t>(counts[q]);
+  const int words_before = static_cast<int>(blockIdx.x) * kUnionBlockThreads;
+  for (int q = tid; q < words_before; q += kUnionBlockThreads) part += flag_count(fw[q]);
   uint32_t base;
   block_scan(part, wave_sums, &base);
   if (tid == 0) base_sh = base;
   __syncthreads();  // wave_sums is reused below
   base = base_sh;
 
-  const int word = blockIdx.x * kUnionBlockThreads + tid;
-  const int n16 = (D + 15) / 16;
-  const uint4 f = word < n16 ? reinterpret_cast<const uint4*>(flags)[word] : make_uint4(0, 0, 0, 0);
+  const int word = words_before + tid;
+  const int n16 = (D + 15) / 16;   // flags past D in the last word are cleared zeros
+  const uint4 f = word < n16 ? fw[word] : make_uint4(0, 0, 0, 0);
   const uint32_t cnt = flag_count(f);
   uint32_t n_block;
   uint32_t pos = block_scan(cnt, wave_sums, &n_block) - cnt;
@@ -579,7 +568,7 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
 int mlp_union_blocks(int D) { return (D + kUnionBlockFlags - 1) / kUnionBlockFlags; }
 
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, int32_t* counts, hipStream_t st) {
+                            uint8_t* flags, hipStream_t st) {
   const int n16 = (D + 15) / 16;
   hipLaunchKernelGGL(sha_mlp_union_clear_kernel, dim3(min((n16 + 255) / 256, 1024)), dim3(256), 0,
                      st, flags, D);
@@ -590,12 +579,8 @@ hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel,
                        0, st, rows, total, D, flags);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int nb = mlp_union_blocks(D);
-  hipLaunchKernelGGL(sha_mlp_union_count_kernel, dim3(nb), dim3(kUnionBlockThreads), 0, st, flags,
-                     D, counts);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sha_mlp_union_write_kernel, dim3(nb), dim3(kUnionBlockThreads), 0, st, flags,
-                     D, counts, sel, n_sel);
+  hipLaunchKernelGGL(sha_mlp_union_write_kernel, dim3(mlp_union_blocks(D)),
+                     dim3(kUnionBlockThreads), 0, st, flags, D, sel, n_sel);
   return hipGetLastError();
 }
 

@@ -278,8 +278,8 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
  * n to *n_sel (device int32).  Deterministic; no host synchronisation.
  *   workspace: caller-owned device buffer of at least
  *              sha_mlp_union_workspace_bytes(D) bytes (one flag byte per
- *              neuron, 256-byte padded, then one count per 4096 neurons),
- *              16-byte aligned; contents on entry do not matter.
+ *              neuron, 256-byte padded), 16-byte aligned; contents on entry
+ *              do not matter.
  * Errors: D < 1, B < 0 or k < 0 -> SHA_ERR_INVALID_ARG; null sel / n_sel
  * (or row_neurons when B*k > 0) -> SHA_ERR_INVALID_ARG; short workspace ->
  * SHA_ERR_WORKSPACE.

@@ -138,8 +138,8 @@ def test_mlp_host_validation():
     assert L.sha_mlp_union(P, 2, 3, 10, None, P, None, P, big) == 1
     assert L.sha_mlp_union(None, 2, 3, 10, P, P, None, P, big) == 1
     assert L.sha_mlp_union(P + 2, 2, 3, 10, P, P, None, P, big) == 3
-    assert L.sha_mlp_union_workspace_bytes(1000) == 1024 + 256     # flags, block counts
-    assert L.sha_mlp_union_workspace_bytes(36864) == 36864 + 256
+    assert L.sha_mlp_union_workspace_bytes(1000) == 1024           # one flag byte per neuron
+    assert L.sha_mlp_union_workspace_bytes(36864) == 36864
     assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, P, 1023) == 4
     assert L.sha_mlp_union(P, 2, 3, 1000, P, P, None, None, big) == 4
 
