@@ -34,7 +34,7 @@ from contextual_head_sparsity_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 CSRC = os.path.join(ROOT, "contextual_head_sparsity_amd", "csrc")
-KERNEL_SOURCES = ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_device.h", "sha_launch.h")
+KERNEL_SOURCES = ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_device.h", "sha_decode.h")
 METRIC = "SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), OPT-66B shape B=64"
 
 

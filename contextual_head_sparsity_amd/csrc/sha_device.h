@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "sha_launch.h"
+#include "sha_decode.h"
 
 namespace sha {
 namespace detail {
