@@ -391,6 +391,9 @@ sha_status check_mlp(int B, int d, int D, int n_max, int dtype) {
   if (dtype != SHA_F16 && dtype != SHA_BF16) return SHA_ERR_UNSUPPORTED;
   if (d % 256 != 0) return SHA_ERR_UNSUPPORTED;
   if (B > 65535 * 64) return SHA_ERR_INVALID_ARG;
+  // The up projection addresses weight rows with 32-bit byte offsets.
+  if (static_cast<uint64_t>(D) * static_cast<uint64_t>(d) * 2u > 0xFFFFFFFFull)
+    return SHA_ERR_UNSUPPORTED;
   return SHA_OK;
 }
 

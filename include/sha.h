@@ -266,7 +266,8 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
  * Weights are stored neuron-major: w1t = W1^T and w2t = W2^T, both [D, d]
  * row-major, so neuron j's input and output weights are rows j.  x and y are
  * [B, d].  f16 and bf16 only (matrix cores; SHA_ERR_UNSUPPORTED otherwise);
- * d must be a multiple of 256 (SHA_ERR_UNSUPPORTED).  Accumulation is fp32;
+ * d must be a multiple of 256 and one weight matrix below 4 GiB
+ * (D * d * 2 < 2^32), else SHA_ERR_UNSUPPORTED.  Accumulation is fp32;
  * relu(x W1[:, S]) is rounded once to the element type before the second
  * product.
  */

@@ -148,6 +148,7 @@ def test_mlp_host_validation():
         return L.sha_selective_mlp(x, w1, w2, sel, n, n_max, B, d, D, y, None, dtype, ws, wsb)
 
     assert mlp(d=200) == 2            # d must be a multiple of 256
+    assert mlp(D=262144, d=8192, n_max=64) == 2   # a 4 GiB weight matrix
     assert mlp(dtype=0) == 2          # f32 has no matrix-core path here
     assert mlp(n_max=1001) == 1       # n_max > D
     assert mlp(B=-1) == 1
