@@ -38,13 +38,22 @@ KERNEL_SOURCES = ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_device.h", "sha_de
 METRIC = "SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), OPT-66B shape B=64"
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed: the hash
+    follows the code, not its documentation."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash() -> str:
-    """Hash of the device sources: counter-derived traffic is only reported
-    for the kernels it was measured on."""
+    """Hash of the decode kernels' sources (code only): counter-derived
+    traffic is only reported for the kernels it was measured on."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

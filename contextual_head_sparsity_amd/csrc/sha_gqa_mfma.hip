@@ -7,7 +7,7 @@
 // (d x heads).  With G = 8 and d = 128 that is 8 flop per K/V byte, which on
 // the vector ALUs costs as much issue time as the HBM stream itself; on MFMA
 // it is a few percent of the matrix-core budget.  The online softmax between
-// the two products is Algorithm 1 steps 7-9 (reproducibility page,
+// the two products is Algorithm 1's tile update (reproducibility page,
 // ri.k117.org, "Pseudocode"), kept per head in base 2 with lazy rescaling.
 //
 // Wave tile: 32 keys.  Operand layouts of v_mfma_f32_16x16x32_{bf16,f16}

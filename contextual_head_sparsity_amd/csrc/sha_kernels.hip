@@ -3,10 +3,10 @@
 // The method: Polar Sparsity reproducibility page (ri.k117.org), "Pseudocode",
 // Algorithm 1 "Selective Head Flash Attention (Decode)": each unit (b, k)
 // resolves head_idx = batch_head_index[b, k], streams K/V of that head in
-// tiles while keeping a running max m, running sum l and output accumulator
-// (steps 3-10), then writes O[b, head_idx, 0, :] (step 11).  Only active heads
-// are read and written (Polar Sparsity notes, papernotes.org, "Selective Head
-// Attention (SHA) Kernel").
+// tiles while keeping a running max m, running sum l and output accumulator,
+// then writes O[b, head_idx, 0, :].  Only active heads are read and written
+// (Polar Sparsity notes, papernotes.org, "Selective Head Attention (SHA)
+// Kernel").
 //
 // MI355X mapping (our design, not the pages' A100 kernel):
 //   * A workgroup is one (unit, KV split).  Inside it, every aligned group of
@@ -22,14 +22,15 @@
 //   * The running max is only moved when a chunk's max exceeds it by more
 //     than kRescaleSlack (base-2 units): probabilities stay <= 2^8, the final
 //     O = o / l is unchanged, and the per-chunk rescale of o is skipped in the
-//     common case.  This is the same running-max algebra as Algorithm 1
-//     step 8 with a lazier update rule.
+//     common case.  This is the same running-max algebra as Algorithm 1's
+//     merge, with a lazier update rule.
 //   * O is accumulated unnormalised and divided by l once at the end (the
-//     value of Algorithm 1 step 9's per-tile normalisation, fewer divides).
+//     value of Algorithm 1's per-tile normalisation, fewer divides).
 //   * KV split (flash-decoding): a unit's keys are cut into nsplit contiguous
 //     chunks so that small B*top_k still fills 256 CUs; each split writes
 //     fp32 (o, m, l) partials and a second kernel merges them in a fixed
-//     order (the step-8 merge across splits).  The kernel boundary makes the
+//     order (the same running-max merge across splits).  The kernel boundary
+//     makes the
 //     partials visible across XCDs without atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -16,9 +16,9 @@
  * head, only active heads are read and written, GQA models use group
  * sparsity), and the Polar Sparsity reproducibility page (ri.k117.org),
  * "Pseudocode", Algorithm 1 "Selective Head Flash Attention (Decode)": a unit
- * (b, k) resolves head_idx = batch_head_index[b, k] (steps 1-2), streams K/V
- * of that head in tiles with a running max / running sum softmax (steps
- * 3-10) and writes O[b, head_idx, 0, :] (step 11).
+ * (b, k) resolves head_idx = batch_head_index[b, k], streams K/V of that
+ * head in tiles with a running max / running sum softmax and writes
+ * O[b, head_idx, 0, :].
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; they must
@@ -139,7 +139,7 @@ sha_status sha_decode_gqa(const void* q, const void* k, const void* v,
  *              clamped.  With an effective split count above 1 the call runs
  *              the split kernel and then a combine kernel that merges the
  *              per-split (o, m, l) partials with the same running-max rule
- *              as Algorithm 1 step 8.
+ *              as Algorithm 1's tile merge.
  *   workspace: device buffer of at least sha_workspace_bytes(...) bytes for
  *              the same arguments (may be null when that is 0), owned by the
  *              caller; its contents on entry do not matter.  Calls that

@@ -15,8 +15,8 @@ What it computes (the plain definition, written out):
     every other output slot is left as it was.  papernotes.org notes,
     "Selective Head Attention (SHA) Kernel" (the kernel takes a batch head
     index tensor and only reads/writes active heads); reproducibility page
-    (ri.k117.org), "Pseudocode", Algorithm 1 steps 1-2 (unit -> (b, k) ->
-    head_idx) and step 11 (write O[b, head_idx, 0, :]).
+    (ri.k117.org), "Pseudocode", Algorithm 1 (each unit resolves its (b, k)
+    pair to head_idx and writes O[b, head_idx, 0, :]).
   * GQA: papernotes.org notes, SHA Kernel bullet "GQA models use group
     sparsity"; atlas.scime.ai summary, "Approach" (routers pick top-k heads
     or GQA groups).  batch_group_index selects KV groups; all G = H/H_kv
