@@ -17,8 +17,8 @@ What it computes (the plain definition, written out):
     index tensor and only reads/writes active heads); reproducibility page
     (ri.k117.org), "Pseudocode", Algorithm 1 (each unit resolves its (b, k)
     pair to head_idx and writes O[b, head_idx, 0, :]).
-  * GQA: papernotes.org notes, SHA Kernel bullet "GQA models use group
-    sparsity"; atlas.scime.ai summary, "Approach" (routers pick top-k heads
+  * GQA: papernotes.org notes, SHA Kernel bullets (GQA models are made
+    sparse per KV group); atlas.scime.ai summary, "Approach" (routers pick top-k heads
     or GQA groups).  batch_group_index selects KV groups; all G = H/H_kv
     query heads of a selected group are computed against that group's K/V.
 
