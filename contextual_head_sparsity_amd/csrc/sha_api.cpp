@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -89,27 +90,71 @@ long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa, int dtype) {
 }
 
 // Split count (flash-decoding split-K over the keys), from measurements on
-// MI355X: a head-indexed workgroup (4 waves, 16 KiB of loads in flight per
-// wave) streams ~22 GB/s, so about one workgroup per CU saturates HBM and
-// splitting further only adds partials and tail; the matrix-core group
-// kernel holds 2 workgroups per CU and has a serial load -> MFMA -> LDS ->
-// MFMA chain per tile, and does best with about four workgroups per CU.
-// No split is shorter than kMinSplitKeys keys.
+// MI355X.  No split is shorter than kMinSplitKeys keys.
+//
+// Head-indexed workgroups (4 waves, 16 KiB of loads in flight per wave)
+// stream ~22 GB/s each, so about one workgroup per CU saturates HBM and
+// splitting further only adds partials and tail.
+//
+// The matrix-core group kernel holds 2 workgroups per CU, and its best split
+// count swings with how the last round of workgroups fills the chip, so it
+// is chosen with a round model of the grid: rounds of up to 2 x CUs
+// resident workgroups, each streaming at most kGqaWgGBs while all of them
+// share kGqaHbmGBs, plus kGqaRoundUs of start-up and drain per round and
+// nothing extra for the combine.  The constants are a fit to 99 timed
+// (shape, split) pairs (8-1024 units, 1 K-32 K keys); its picks are within
+// ~2% of the best measured split on average.
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 64;
+constexpr double kGqaHbmGBs = 6800.0;
+constexpr double kGqaWgGBs = 20.0;
+constexpr double kGqaRoundUs = 4.0;
+
+void split_geometry(int Nkv, int nsplit_req, int page, int* nsplit, int* chunk);
+
+// Modelled time (us) of the group kernel with `ns` splits.
+double gqa_round_model_us(long long wgs, int Nkv, int d, int ns, int cus, int* ns_eff) {
+  int chunk = Nkv;
+  split_geometry(Nkv, ns, 0, ns_eff, &chunk);
+  const long long T = wgs * *ns_eff;
+  const long long slots = 2LL * cus;
+  const double bytes = 4.0 * chunk * d;  // K + V rows of one workgroup, 16-bit
+  const double full_rate = std::min(kGqaHbmGBs, kGqaWgGBs * static_cast<double>(slots));
+  const long long full = T / slots, rem = T % slots;
+  double t = static_cast<double>(full) *
+             (bytes * static_cast<double>(slots) / full_rate / 1e3 + kGqaRoundUs);
+  if (rem > 0) {
+    const double rate = std::min(kGqaWgGBs, kGqaHbmGBs / static_cast<double>(rem));
+    t += bytes / rate / 1e3 + kGqaRoundUs;
+  }
+  return t;
+}
 
 int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
                 int num_cus) {
-  (void)d;
   const long long wgs = wgs_per_split(B, H, H_kv, top_k, gqa, dtype);
   if (wgs <= 0) return 1;
+  const int cus = device_cus(num_cus);
   const bool mfma = gqa && H / H_kv > 1 && gqa_mfma(dtype);
-  const long long target = (mfma ? 4LL : 1LL) * device_cus(num_cus);
-  long long ns = (target + wgs - 1) / wgs;
-  const long long max_ns = Nkv / kMinSplitKeys > 1 ? Nkv / kMinSplitKeys : 1;
-  if (ns > max_ns) ns = max_ns;
-  if (ns > kMaxSplits) ns = kMaxSplits;
-  if (ns < 1) ns = 1;
+  long long max_ns = Nkv / kMinSplitKeys > 1 ? Nkv / kMinSplitKeys : 1;
+  if (max_ns > kMaxSplits) max_ns = kMaxSplits;
+  long long ns = 1;
+  if (mfma) {
+    double best = 0.0;
+    for (int c = 1; c <= max_ns; ++c) {
+      int eff = 1;
+      const double t = gqa_round_model_us(wgs, Nkv, d, c, cus, &eff);
+      if (eff != c) continue;  // same geometry as a smaller request
+      if (c == 1 || t < best) {
+        best = t;
+        ns = c;
+      }
+    }
+  } else {
+    ns = (cus + wgs - 1) / wgs;
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+  }
   const int env = env_int("SHA_NSPLIT", 0);
   if (env > 0) ns = env;
   return static_cast<int>(ns);

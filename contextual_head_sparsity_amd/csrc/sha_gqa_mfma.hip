@@ -15,8 +15,13 @@
 //   A[i][k] : lane holds i = c, k = 8q .. 8q+7
 //   B[k][j] : lane holds j = c, k = 8q .. 8q+7
 //   D[i][j] : lane holds i = 4q .. 4q+3, j = c
-// QK: A = K rows (keys 16*mb + c, d = 32*kc + 8q ..) straight from HBM with
-// 128-bit loads, B = Q^T (head c, same d range) held in registers.
+// QK: A = K rows (keys 16*mb + c, d = 32*kc + 8q ..), B = Q^T (head c, same
+// d range) held in registers.  Loading A straight from HBM would make every
+// wave load touch 16 rows x 64 bytes, a pattern that streams markedly slower
+// on this GPU than whole 1 KiB runs; so the K tile is loaded like V (1 KiB
+// contiguous per wave load) into LDS rows padded by 16 bytes, where the 16
+// lanes of each 128-bit read phase (rows c = 0..15, one pitch apart) fall on
+// distinct banks, and read back in the A layout.
 // The D layout leaves each lane with 4 keys (4q + r) of head c per 16-key
 // block; the PV product's K index is ordered so that lane (q, c) owns keys
 // {4q .. 4q+3, 16+4q .. 16+4q+3} of head c, which is exactly what the
@@ -130,8 +135,11 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   constexpr int VLD = kTileKeys * ROWB / 1024;  // 128-bit V loads per lane per tile
   constexpr int LPRW = ROWB / 16;            // lanes per V row in a load
   static_assert(kCols * D * 4 + kCols * 2 * 4 <= VBUF, "partial O must fit the V buffer");
+  constexpr int KPITCH = ROWB + 16;          // K rows: conflict-free 128-bit operand reads
+  constexpr int KBUF = kTileKeys * KPITCH;
 
   __shared__ __attribute__((aligned(16))) char smem[WAVES * VBUF];
+  __shared__ __attribute__((aligned(16))) char smem_k[WAVES * KBUF];
   __shared__ int sm_pages[LAYOUT == kKvPaged ? kMaxSplitPages : 1];
 
   const int tid = threadIdx.x;
@@ -174,18 +182,17 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   // compiler orders the V-tile stores against the transposed reads.
   lds_char_t* const sbase = (lds_char_t*)(smem);
   lds_char_t* const vt = sbase + wave * VBUF;
+  lds_char_t* const kt = (lds_char_t*)(smem_k) + wave * KBUF;
 
   for (int base = ks + wave * kTileKeys; base < ke; base += WAVES * kTileKeys) {
     const bool full = base + kTileKeys <= ke;
-    // K tile straight into A operands.
-    uint4 kr[2][KC];
+    // K tile: 1 KiB contiguous per wave load, like V.
+    uint4 kl[VLD];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      int row = base + 16 * mb + col;
+    for (int u = 0; u < VLD; ++u) {
+      int row = base + u * (1024 / ROWB) + lane / LPRW;
       if (!full) row = min(row, ke - 1);
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        kr[mb][kc] = ld16_stream(rows.k(row) + kc * 64 + q4 * 16);
+      kl[u] = ld16_stream(rows.k(row) + (lane % LPRW) * 16);
     }
     // V tile: 1 KiB contiguous per wave load.
     uint4 vr[VLD];
@@ -196,6 +203,18 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
       vr[u] = ld16_stream(rows.v(row) + (lane % LPRW) * 16);
     }
 
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const int rr = u * (1024 / ROWB) + lane / LPRW;
+      *(lds_u32x4_t*)(kt + rr * KPITCH + (lane % LPRW) * 16) = __builtin_bit_cast(u32x4_t, kl[u]);
+    }
+    uint4 kr[2][KC];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kr[mb][kc] = __builtin_bit_cast(
+            uint4, *(lds_u32x4_t*)(kt + (16 * mb + col) * KPITCH + kc * 64 + q4 * 16));
     // Scores S^T = K Q^T: lane holds keys 16*mb + 4*q4 + r of head col.
     f32x4 s[2];
 #pragma unroll
