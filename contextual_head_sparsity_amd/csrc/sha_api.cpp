@@ -366,56 +366,40 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Grid sizes from the selection bound.  Both products stream weights, so the
 // planner fills the chip without leaving a small second round of work.
-//   up  : one workgroup per 64 selected neurons x 64 batch rows (2 resident
-//         per CU); its K (d) is split in whole 256-k stages.  A grid that
-//         fills half to all of the resident slots runs unsplit; a smaller
-//         one is split until it fills about half of them (at most 8 ways); a
-//         larger one takes 2 or 3 splits, whichever gives the fewer rounds of
-//         resident workgroups per unit of work after the cost of the fp32
-//         partials each split writes and the finalize reads back.
+//   up  : one workgroup per kMlpUpNeurons selected neurons x 64 batch rows
+//         (2 resident per CU); its K (d) is split in whole kMlpUpKc stages,
+//         ceil(0.95 x resident slots / workgroups) ways (at most 8).
 //   down: one workgroup per 256 output columns x 64 rows; the neuron range is
 //         split for about two workgroups per CU (each range keeps >= 64
 //         neurons, at most 64 splits).
 // The constants come from split sweeps of the OPT MLPs on MI355X.
 constexpr int kUpWgsPerCu = 2;
+constexpr int kMaxUpSplits = 8;
 constexpr int kDownWgsPerCu = 2;
 
-int up_split_count(long long items, int kstages, int b_pad, int d, int cus) {
+int up_split_count(long long items, int kstages, int cus) {
+  // The K splits bring the grid to about one round of resident workgroups
+  // (fewer leave HBM idle: 288 unsplit OPT-66B workgroups stream 3.8 TB/s);
+  // a grid already past that takes no splits beyond it.
   const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
-  int us = 1;
-  if (2 * items < slots) {
-    us = static_cast<int>(slots / (2 * items));
-    if (us > 8) us = 8;
-  } else if (items > slots) {
-    double best_cost = 0.0;
-    for (int cand = 2; cand <= 3; ++cand) {
-      const long long rounds = (items * cand + slots - 1) / slots;
-      // Unit: one round of full-K workgroups.  Partials: cand x (b_pad x n)
-      // fp32 written and read, against slots x 64 x d 16-bit weights per round.
-      const double partial = static_cast<double>(cand) * items * 64 * b_pad * 8 /
-                             (static_cast<double>(slots) * 64 * d * 2);
-      const double cost = static_cast<double>(rounds) / cand + partial;
-      if (cand == 2 || cost < best_cost) {
-        us = cand;
-        best_cost = cost;
-      }
-    }
-  }
+  long long us = (slots * 95 / 100 + items - 1) / items;
+  if (us > kMaxUpSplits) us = kMaxUpSplits;
   if (us > kstages) us = kstages;
-  return us < 1 ? 1 : us;
+  return us < 1 ? 1 : static_cast<int>(us);
 }
 
 MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   MlpPlan p{};
   const int cus = device_cus(num_cus);
-  p.n_pad = ((n_max > 0 ? n_max : 1) + 63) / 64 * 64;
+  constexpr int NU = sha::kMlpUpNeurons;
+  p.n_pad = ((n_max > 0 ? n_max : 1) + NU - 1) / NU * NU;
   p.b_pad = (B + 63) / 64 * 64;
-  const long long up_items = static_cast<long long>(p.n_pad / 64) * (p.b_pad / 64);
-  const int kstages = d / 256;
-  int us = up_split_count(up_items, kstages, p.b_pad, d, cus);
+  const long long up_items = static_cast<long long>(p.n_pad / NU) * (p.b_pad / 64);
+  const int kstages = d / sha::kMlpUpKc;
+  int us = up_split_count(up_items, kstages, cus);
   if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
   if (us > kstages) us = kstages;
-  p.up_kper = (kstages + us - 1) / us * 256;
+  p.up_kper = (kstages + us - 1) / us * sha::kMlpUpKc;
   p.up_splits = (d + p.up_kper - 1) / p.up_kper;
   const long long dn_items = static_cast<long long>(d / 256) * (p.b_pad / 64);
   long long ds = static_cast<long long>(kDownWgsPerCu) * cus / dn_items;

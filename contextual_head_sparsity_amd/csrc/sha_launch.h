@@ -13,6 +13,10 @@ namespace sha {
 
 // Selective MLP (batch union of active neurons).  Sizes validated on the host;
 // the selection count is device data, clamped to n_max by the kernels.
+// Up-projection tile: kMlpUpNeurons selected neurons x 64 batch rows per
+// workgroup, in K stages of kMlpUpKc.
+constexpr int kMlpUpNeurons = 128;
+constexpr int kMlpUpKc = 128;
 struct MlpArgs {
   const void* x;        // [B, d]
   const void* w1t;      // [D, d]  (W1^T, neuron-major)
@@ -24,7 +28,7 @@ struct MlpArgs {
   float* up_part;       // workspace: up-projection K-split partials [up_splits, b_pad, n_pad]
   float* dn_part;       // workspace: down-projection split partials [dn_splits, b_pad, d]
   int B, d, D, n_max;
-  int n_pad, b_pad;     // n_max rounded up to 64, B rounded up to 64
+  int n_pad, b_pad;     // n_max rounded up to kMlpUpNeurons, B rounded up to 64
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
 };

@@ -15,8 +15,8 @@
 //            output offset), writes its marked neurons in ascending order,
 //            and the last block writes the total (deterministic, on device).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
-//            a workgroup owns 64 selected neurons x 64 batch rows over a K
-//            range; weight rows stream in 512-byte runs (non-temporal
+//            a workgroup owns 128 selected neurons x 64 batch rows over a K
+//            range; weight rows stream in 256-byte runs (non-temporal
 //            128-bit loads, two stages ahead) through swizzled LDS into A
 //            operands, x pieces come from L2 as B operands.  With one K
 //            split it applies ReLU and writes H (16-bit); with several it
@@ -199,25 +199,31 @@ __device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
   return r >= 0 && r < a.D;
 }
 
-// A workgroup owns 64 selected neurons x 64 batch rows over a K range, in
-// stages of kUpKc = 256 k.  Each stage's weights (64 rows x 512 B) are read
-// with 128-bit non-temporal loads, two rows of 512 contiguous bytes per wave
-// instruction, three stages ahead of their use (two register sets: a set is
-// reloaded as soon as it is written to LDS), and written one stage ahead
-// into a double-buffered LDS tile with an XOR
+// A workgroup owns kUpN = 128 selected neurons x 64 batch rows over a K
+// range, in stages of kUpKc = 128 k.  Each stage's weights (128 rows x
+// 256 B) are read with 128-bit non-temporal loads, four rows of 256
+// contiguous bytes per wave instruction, three stages ahead of their use
+// (two register sets: a set is reloaded as soon as it is written to LDS),
+// and written one stage ahead into a double-buffered LDS tile with an XOR
 // swizzle of the 16-byte pieces (slot = piece ^ (row & 15)), so that the
 // A-operand reads (16 rows x one piece per quarter wave) hit distinct banks;
 // one barrier per stage both publishes the next tile and retires the one
-// just read.  Wave w multiplies all 64 neurons by batch block w: its x pieces
-// (B operands) come from L2 into registers one stage ahead, and no two waves
-// read the same x.  Each step issues its x loads before its weight loads:
-// waiting for a stage's x then leaves the younger weight stages in flight
-// (loads complete in order).
+// just read.  Wave w multiplies all 128 neurons by batch block w: its x
+// pieces (B operands) come from L2 into registers one stage ahead, and no two
+// waves read the same x.  Every x byte read serves 128 neurons: x comes from
+// L2 at half the weight bytes (at 64 neurons per workgroup it matched them
+// and cost about a fifth of the kernel's time).  Each step issues its x
+// loads before its weight loads: waiting for a stage's x then leaves the
+// younger weight stages in flight (loads complete in order).
 // Workgroup id = ((btile * up_splits) + split) * nblocks + nblock.
-constexpr int kUpKc = 256;                  // k per stage
+constexpr int kUpN = kMlpUpNeurons;         // neurons per workgroup
+constexpr int kUpNB = kUpN / 16;            // MFMA neuron blocks
+constexpr int kUpKc = kMlpUpKc;             // k per stage
 constexpr int kUpRowB = kUpKc * 2;          // bytes of one weight row per stage
-constexpr int kUpLoads = 64 * kUpRowB / 16 / 256;  // 16-byte weight pieces per thread per stage
+constexpr int kUpPieces = kUpRowB / 16;     // 16-byte pieces per row per stage
+constexpr int kUpLoads = kUpN * kUpPieces / 256;  // weight pieces per thread per stage
 constexpr int kUpX = kUpKc / 32;            // x pieces (MFMA K steps) per lane per stage
+static_assert(kUpPieces == 16, "the swizzle and the row mapping assume 16 pieces per row");
 
 struct UpW {
   uint4 v[kUpLoads];
@@ -229,15 +235,15 @@ struct UpX {
 template <int DT>
 __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
-  __shared__ __attribute__((aligned(16))) char wsm_[2 * 64 * kUpRowB];
-  const int nblocks = a.n_pad / 64;
+  __shared__ __attribute__((aligned(16))) char wsm_[2 * kUpN * kUpRowB];
+  const int nblocks = a.n_pad / kUpN;
   int t = blockIdx.x;
   const int nblk = t % nblocks;
   t /= nblocks;
   const int split = t % a.up_splits;
   const int btile = t / a.up_splits;
   const int n_sel = sel_count(a);
-  const int n0 = nblk * 64;
+  const int n0 = nblk * kUpN;
   if (n0 >= n_sel) return;                    // whole workgroup: past the selection
   const int b0 = btile * 64;
   const int kbeg = split * a.up_kper;
@@ -248,8 +254,8 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   const int q4 = lane >> 4, c = lane & 15;
   lds_char_t* const wl = (lds_char_t*)(wsm_);
 
-  // Weight pieces of this thread: piece index p = tid + 256 i -> row p >> 5
-  // (= (tid >> 5) + 8 i), 16-byte column p & 31; 32-bit byte offsets of the
+  // Weight pieces of this thread: piece index p = tid + 256 i -> row p >> 4
+  // (= (tid >> 4) + 16 i), 16-byte column p & 15; 32-bit byte offsets of the
   // rows (one weight matrix is below 4 GiB, checked on the host) and the LDS
   // slot of each piece.
   const char* w1 = static_cast<const char*>(a.w1t) + static_cast<size_t>(kbeg) * 2;
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   int wdst[kUpLoads];
 #pragma unroll
   for (int i = 0; i < kUpLoads; ++i) {
-    const int r = (tid >> 5) + 8 * i, col = tid & 31;
+    const int r = (tid >> 4) + 16 * i, col = tid & 15;
     const int row = sel_row(a, min(n0 + r, n_sel - 1));
     woff[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) * 2u + col * 16;
     wdst[i] = r * kUpRowB + ((col ^ (r & 15)) * 16);
@@ -268,9 +274,9 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   const char* xsrc = static_cast<const char*>(a.x) +
                      (static_cast<size_t>(xok ? b : a.B - 1) * a.d + kbeg + 8 * q4) * 2;
 
-  f32x4 acc[4];  // [neuron block]; batch block = wave
+  f32x4 acc[kUpNB];  // [neuron block]; batch block = wave
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kUpNB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto load_w = [&](int st, UpW& d) {
 #pragma unroll
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   };
   const uint32_t xmask = xok ? 0xFFFFFFFFu : 0u;
   auto write_w = [&](int st, const UpW& w) {
-    lds_char_t* const buf = wl + (st & 1) * (64 * kUpRowB);
+    lds_char_t* const buf = wl + (st & 1) * (kUpN * kUpRowB);
 #pragma unroll
     for (int i = 0; i < kUpLoads; ++i)
       *(lds_u32x4_t*)(buf + wdst[i]) = __builtin_bit_cast(u32x4_t, w.v[i]);
@@ -297,14 +303,14 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     if (!C || st + 1 < nst) write_w(st + 1, wnext);
     if (!C || st + 1 < nst) load_x(st + 1, xnext);
     if (!C || st + 3 < nst) load_w(st + 3, wnext);
-    const lds_char_t* const buf = wl + (st & 1) * (64 * kUpRowB);
+    const lds_char_t* const buf = wl + (st & 1) * (kUpN * kUpRowB);
 #pragma unroll
     for (int s = 0; s < kUpX; ++s) {
       const uint4 xv = xcur.v[s];
       const uint4 xb = make_uint4(xv.x & xmask, xv.y & xmask, xv.z & xmask, xv.w & xmask);
       const int piece = 4 * s + q4;         // 16-byte piece of the row this lane reads
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < kUpNB; ++mb) {
         const u32x4_t av = *(const lds_u32x4_t*)(buf + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
         acc[mb] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[mb]);
       }
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
 
   // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad: padded rows get zeros)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < kUpNB; ++mb) {
     const int nbase = n0 + 16 * mb + 4 * q4;
     // Entries outside [0, D) (and past the count) produce no activation.
 #pragma unroll
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
 template <int DT>
 hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
-  const long long up_wgs = static_cast<long long>(a.n_pad / 64) * a.up_splits * btiles;
+  const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
   hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
                      st, a);
   hipError_t e = hipGetLastError();

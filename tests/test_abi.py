@@ -170,19 +170,19 @@ def test_mlp_host_validation():
 def test_mlp_workspace_accounting():
     L = bd.lib()
     # OPT-66B MLP, all 36864 neurons selected, 64 rows, 256 CUs: H (64 x 36864
-    # 16-bit), the up projection's fp32 partials over 3 K splits (576
-    # workgroups exceed the 512 resident slots; 3 splits give 4 rounds of
-    # 1/3-size work) and the down projection's over 14 neuron splits (36
-    # column blocks x 14 ~ 2 workgroups per CU).
+    # 16-bit), the up projection's fp32 partials over 2 K splits (288
+    # workgroups of 128 neurons; 2 splits bring them to about one round of
+    # the 512 resident slots) and the down projection's over 14 neuron splits
+    # (36 column blocks x 14 ~ 2 workgroups per CU).
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 36864, 256)
-    assert ws == 64 * 36864 * 2 + 3 * 64 * 36864 * 4 + 14 * 64 * 9216 * 4
-    # 21056 padded neurons (329 workgroups: half to all of the slots): no split
+    assert ws == 64 * 36864 * 2 + 2 * 64 * 36864 * 4 + 14 * 64 * 9216 * 4
+    # 21120 padded neurons (165 workgroups): 3 K splits (3072-element ranges)
     ws = L.sha_selective_mlp_workspace_bytes(8, 9216, 36864, 21033, 256)
-    assert ws == 64 * 21056 * 2 + 14 * 64 * 9216 * 4
-    # a 64-neuron selection splits the up projection's K 8 ways (1280-element
-    # ranges: 8 splits) and keeps a single down split
+    assert ws == 64 * 21120 * 2 + 3 * 64 * 21120 * 4 + 14 * 64 * 9216 * 4
+    # a 64-neuron selection (one 128-neuron workgroup) splits the up
+    # projection's K 8 ways (1152-element ranges) and keeps a single down split
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
-    assert ws == 64 * 64 * 2 + 8 * 64 * 64 * 4
+    assert ws == 64 * 128 * 2 + 8 * 64 * 128 * 4
 
 
 def test_router_host_validation():
