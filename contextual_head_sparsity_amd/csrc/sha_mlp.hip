@@ -422,56 +422,66 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
 
   // Gathered W2t rows of a chunk: 64 rows x 512 B = 2048 pieces (8 per
   // thread); H chunk: 64 rows x 128 B = 512 pieces (2 per thread), neurons at
-  // or past nend read as zero.
+  // or past nend read as zero.  Piece tid + 256 i of the weights is row
+  // 2 wave + (lane >> 5) + 8 i, so each load instruction needs two selection
+  // entries that are the same for the whole wave: they are read with scalar
+  // loads (own counter), and the vector loads of earlier chunks need not
+  // complete before the next chunk's addresses are known.  H pieces are read
+  // unconditionally (offsets clamped inside the row) and masked only when
+  // they are written to LDS: masking at load time would make the wave wait
+  // for them, and (loads complete in order) for every older load, at once.
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const bool upper = lane >= 32;
   auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[2]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 5, piece = idx & 31;
-      const int row = sel_row(a, min(k0 + r, nend - 1));
+      const int r0 = k0 + 2 * wu + 8 * i;
+      const int s0 = a.sel[min(r0, nend - 1)], s1 = a.sel[min(r0 + 1, nend - 1)];
+      const int row0 = (s0 >= 0 && s0 < a.D) ? s0 : 0, row1 = (s1 >= 0 && s1 < a.D) ? s1 : 0;
+      const int row = upper ? row1 : row0;
       wv[i] = ld16_stream(static_cast<const char*>(a.w2t) +
-                          (static_cast<size_t>(row) * a.d + col0 + piece * 8) * 2);
+                          (static_cast<size_t>(row) * a.d + col0 + (lane & 31) * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, piece = idx & 7;
-      const int nn = k0 + piece * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const char* src = static_cast<const char*>(a.h) + (static_cast<size_t>(b0 + r) * a.n_pad + nn) * 2;
-      if (nn + 8 <= nend) {
-        v = ld16(src);
-      } else if (nn < nend) {
-        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
-        uint16_t t[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t[e] = (nn + e < nend) ? s16[e] : 0;
-        v = make_uint4(t[0] | (uint32_t(t[1]) << 16), t[2] | (uint32_t(t[3]) << 16),
-                       t[4] | (uint32_t(t[5]) << 16), t[6] | (uint32_t(t[7]) << 16));
-      }
-      hv[i] = v;
+      const int nc = min(k0 + piece * 8, a.n_pad - 8);  // past n_pad: past nend, masked
+      hv[i] = ld16(static_cast<const char*>(a.h) +
+                   (static_cast<size_t>(b0 + r) * a.n_pad + nc) * 2);
     }
   };
 
-  // Software pipeline: chunk i+1 is in flight while chunk i is multiplied.
-  uint4 wcur[8], hcur[2], wnext[8], hnext[2];
-  if (nbeg < nend) load_chunk(nbeg, wcur, hcur);
-  for (int k0 = nbeg; k0 < nend; k0 += kDnKc) {
-    const bool more = k0 + kDnKc < nend;
-    if (more) load_chunk(k0 + kDnKc, wnext, hnext);
+  // Chunk j (neurons nbeg + 64 j ..) lives in register set j % 2.  Step j:
+  // wait for the previous chunk's LDS reads, write chunk j to LDS, reload its
+  // set with chunk j + 2 (two chunks in flight during the products), publish
+  // and multiply.  CHECK: only load inside the range.
+  const int nch = nend > nbeg ? (nend - nbeg + kDnKc - 1) / kDnKc : 0;
+  auto step = [&](int j, uint4 (&w)[8], uint4 (&h)[2], auto check) {
+    constexpr bool C = decltype(check)::value;
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 5, piece = idx & 31;
-      *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, wcur[i]);
+      *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, w[i]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, piece = idx & 7;
-      *(lds_u32x4_t*)(hl + r * kDnHPitch + piece * 16) = __builtin_bit_cast(u32x4_t, hcur[i]);
+      const int cnt = min(max(nend - (nbeg + j * kDnKc + piece * 8), 0), 8);  // valid neurons
+      uint32_t m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        m[e] = (2 * e < cnt ? 0x0000FFFFu : 0u) | (2 * e + 1 < cnt ? 0xFFFF0000u : 0u);
+      const u32x4_t hm = {h[i].x & m[0], h[i].y & m[1], h[i].z & m[2], h[i].w & m[3]};
+      *(lds_u32x4_t*)(hl + r * kDnHPitch + piece * 16) = hm;
     }
+    if (!C || j + 2 < nch) load_chunk(nbeg + (j + 2) * kDnKc, w, h);
+    // Keep the loads ahead of the products: the scheduler would otherwise
+    // spread them among the MFMAs and wait for them there.
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < kDnKc / 32; ++ks) {
@@ -496,12 +506,29 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
         for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = M::mma(ha[mb], wb, acc[mb][nb]);
       }
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wcur[i] = wnext[i];
-      hcur[0] = hnext[0];
-      hcur[1] = hnext[1];
+  };
+
+  if (nch > 0) {
+    // Both sets are loaded on every path into the loop (a one-chunk range
+    // loads its chunk twice), so the compiler sees the same loads in flight
+    // at the loop head from the entry and from the back edge and can leave
+    // the younger set in flight; a conditional second load makes it wait
+    // for everything there.
+    uint4 wa[8], ha0[2], wb8[8], hb0[2];
+    load_chunk(nbeg, wa, ha0);
+    load_chunk(nbeg + min(1, nch - 1) * kDnKc, wb8, hb0);
+    using Chk = std::true_type;
+    using NoChk = std::false_type;
+    int j = 0;
+    for (; j + 4 <= nch; j += 2) {
+      step(j, wa, ha0, NoChk{});
+      step(j + 1, wb8, hb0, NoChk{});
     }
+    for (; j + 2 <= nch; j += 2) {
+      step(j, wa, ha0, Chk{});
+      step(j + 1, wb8, hb0, Chk{});
+    }
+    if (j < nch) step(j, wa, ha0, Chk{});
   }
 
   // lane holds y[b = b0 + 16 mb + 4 q4 + r][col = col0 + 64 wave + 16 nb + c]
