@@ -268,7 +268,10 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     woff[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) * 2u + col * 16;
     wdst[i] = r * kUpRowB + ((col ^ (r & 15)) * 16);
   }
-  // x row of this lane (padding rows past B read row B - 1 and use zeros).
+  // x row of this lane.  Padding rows past B read row B - 1: their H rows
+  // are finite and no output row reads them (the down projection stores only
+  // rows < B), so x is not masked (a mask applied to freshly loaded x made
+  // the wave wait for the weight loads in flight before it).
   const int b = b0 + 16 * wave + c;
   const bool xok = b < a.B;
   const char* xsrc = static_cast<const char*>(a.x) +
@@ -286,7 +289,6 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
 #pragma unroll
     for (int s = 0; s < kUpX; ++s) d.v[s] = ld16(xsrc + st * kUpRowB + s * 64);
   };
-  const uint32_t xmask = xok ? 0xFFFFFFFFu : 0u;
   auto write_w = [&](int st, const UpW& w) {
     lds_char_t* const buf = wl + (st & 1) * (kUpN * kUpRowB);
 #pragma unroll
@@ -302,12 +304,16 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     constexpr bool C = decltype(check)::value;
     if (!C || st + 1 < nst) write_w(st + 1, wnext);
     if (!C || st + 1 < nst) load_x(st + 1, xnext);
+    // x before the weights, as written: the scheduler may otherwise sink the
+    // x loads below them, and the next step's wait for x would then wait for
+    // the weights as well.
+    __builtin_amdgcn_sched_barrier(0);
     if (!C || st + 3 < nst) load_w(st + 3, wnext);
     const lds_char_t* const buf = wl + (st & 1) * (kUpN * kUpRowB);
 #pragma unroll
     for (int s = 0; s < kUpX; ++s) {
       const uint4 xv = xcur.v[s];
-      const uint4 xb = make_uint4(xv.x & xmask, xv.y & xmask, xv.z & xmask, xv.w & xmask);
+      const uint4 xb = xv;
       const int piece = 4 * s + q4;         // 16-byte piece of the row this lane reads
 #pragma unroll
       for (int mb = 0; mb < kUpNB; ++mb) {
@@ -318,32 +324,36 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     __syncthreads();
   };
 
-  UpW wa, wb;
-  UpX x0, x1;
   if (nst > 0) {
+    // The prologue loads the same sets on every path into the loop (short
+    // ranges load their last stage again): with conditional loads here the
+    // compiler cannot tell which loads are still in flight at the loop head
+    // and waits for all of them there, once per pass.
+    UpW wa, wb;
+    UpX x0, x1;
     load_x(0, x0);
     load_w(0, wa);
+    load_w(min(1, nst - 1), wb);
+    write_w(0, wa);
+    load_w(min(2, nst - 1), wa);
+    __syncthreads();
+    // Two steps per pass; passes whose look-ahead work all lies inside the K
+    // range run without checks.
+    using Chk = std::true_type;
+    using NoChk = std::false_type;
+    int st = 0;
+    for (; st + 5 <= nst; st += 2) {
+      step(st, wb, x0, x1, NoChk{});
+      step(st + 1, wa, x1, x0, NoChk{});
+    }
+    for (; st + 2 <= nst; st += 2) {
+      step(st, wb, x0, x1, Chk{});
+      step(st + 1, wa, x1, x0, Chk{});
+    }
+    if (st < nst) step(st, wb, x0, x1, Chk{});
   }
-  if (nst > 1) load_w(1, wb);
-  if (nst > 0) write_w(0, wa);
-  if (nst > 2) load_w(2, wa);
-  __syncthreads();
-  // Two steps per pass; passes whose look-ahead work all lies inside the K
-  // range run without checks.
-  using Chk = std::true_type;
-  using NoChk = std::false_type;
-  int st = 0;
-  for (; st + 5 <= nst; st += 2) {
-    step(st, wb, x0, x1, NoChk{});
-    step(st + 1, wa, x1, x0, NoChk{});
-  }
-  for (; st + 2 <= nst; st += 2) {
-    step(st, wb, x0, x1, Chk{});
-    step(st + 1, wa, x1, x0, Chk{});
-  }
-  if (st < nst) step(st, wb, x0, x1, Chk{});
 
-  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad: padded rows get zeros)
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad)
 #pragma unroll
   for (int mb = 0; mb < kUpNB; ++mb) {
     const int nbase = n0 + 16 * mb + 4 * q4;
