@@ -60,6 +60,7 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) float lds_float_t;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 
 template <int DT>
 struct Mma;
@@ -134,7 +135,8 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   constexpr int VBUF = kTileKeys * PITCH;    // LDS bytes per wave (V tile, later the partial O)
   constexpr int VLD = kTileKeys * ROWB / 1024;  // 128-bit V loads per lane per tile
   constexpr int LPRW = ROWB / 16;            // lanes per V row in a load
-  static_assert(kCols * D * 4 + kCols * 2 * 4 <= VBUF, "partial O must fit the V buffer");
+  constexpr int PO = D + 4;                  // partial-O row pitch (floats): conflict-free writes
+  static_assert(kCols * PO * 4 + kCols * 2 * 4 <= VBUF, "partial O must fit the V buffer");
   constexpr int KPITCH = ROWB + 16;          // K rows: conflict-free 128-bit operand reads
   constexpr int KBUF = kTileKeys * KPITCH;
 
@@ -275,13 +277,14 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // Partial O^T of this wave into its own LDS buffer: [head][d], then (m, l).
+  // Partial O^T of this wave into its own LDS buffer: [head][d] with rows
+  // PO floats apart (PO = 4 mod 64 words: the 16 heads of a 128-bit write
+  // pass fall on distinct banks), then (m, l).
   lds_float_t* po = (lds_float_t*)(vt);
-  lds_float_t* pml = po + kCols * D;
+  lds_float_t* pml = po + kCols * PO;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) po[col * D + db * 16 + 4 * q4 + r] = acc[db][r];
+    *(lds_f32x4_t*)(po + col * PO + db * 16 + 4 * q4) = acc[db];
   if (q4 == 0) {
     pml[2 * col] = m;
     pml[2 * col + 1] = lsum;
@@ -294,15 +297,15 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
     float Mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w)
-      Mx = fmaxf(Mx, ((const lds_float_t*)(sbase + w * VBUF))[kCols * D + 2 * j]);
+      Mx = fmaxf(Mx, ((const lds_float_t*)(sbase + w * VBUF))[kCols * PO + 2 * j]);
     const float Mu = (Mx == kNegInf) ? 0.f : Mx;
     float L = 0.f, accv = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
       const lds_float_t* pw = (const lds_float_t*)(sbase + w * VBUF);
-      const float wt = exp2_hw(pw[kCols * D + 2 * j] - Mu);
-      L += wt * pw[kCols * D + 2 * j + 1];
-      accv += wt * pw[j * D + c];
+      const float wt = exp2_hw(pw[kCols * PO + 2 * j] - Mu);
+      L += wt * pw[kCols * PO + 2 * j + 1];
+      accv += wt * pw[j * PO + c];
     }
     const int h = g * a.G + head0 + j;
     if (a.nsplit == 1) {
