@@ -402,7 +402,10 @@ class DecodeStep:
     layers: list of dicts with device tensors under the sha_step_layer field
     names (router_x, router_w, router_bias, router_scores, index, q, k, v, o,
     dense, mlp_x, mlp_w1t, mlp_w2t, mlp_y, mlp_rows) and optionally
-    seqlens (per-row key counts; k/v must then be [B, H_kv, Nkv, d] views).
+    seqlens (per-row key counts) and block_table (a paged layer: k/v are
+    [num_pages, H_kv, page, d] views of page pools and block_table is the
+    [B, max_pages] int32 table, as for sha_decode_paged; Nkv is then the
+    longest row).
     The tensors are referenced for the life of the step: refresh their
     contents in place between runs.
     """
@@ -425,9 +428,9 @@ class DecodeStep:
                     self._keep.append(t)
                 setattr(arr[i], name, _ptr(t))
             arr[i].dense = int(bool(L.get("dense", False)))
-            k, v, sl = L["k"], L["v"], L.get("seqlens")
-            if sl is not None or not (k.is_contiguous() and v.is_contiguous()):
-                lay, keep = _layout(k, v, sl, None, B, Nkv)
+            k, v, sl, bt = L["k"], L["v"], L.get("seqlens"), L.get("block_table")
+            if sl is not None or bt is not None or not (k.is_contiguous() and v.is_contiguous()):
+                lay, keep = _layout(k, v, sl, bt, B, Nkv)
                 self._keep += [lay] + list(keep)
                 arr[i].kv = ctypes.pointer(lay)
         self._keep.append(arr)

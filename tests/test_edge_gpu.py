@@ -97,14 +97,29 @@ def test_head_level_shared_kv():
     _run_check(w, q, k, v, idx, o)
 
 
-@pytest.mark.parametrize("G", [2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("G", [2, 3, 4, 5, 8, 16, 17, 32, 64])
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 def test_gqa_group_sizes(G, dtype):
+    # Groups past 16 heads (the matrix-core kernel's columns per workgroup)
+    # or 8 heads (the f32 kernel's) are cut into several head chunks, the
+    # last one ragged for G = 17; 64 is the largest group the library takes.
     say(f"[edge] gqa G={G} {dtype}")
     H_kv = 3
     w, q, k, v, idx, o = _case(dtype=dtype, B=2, H=G * H_kv, H_kv=H_kv, top_k=2, Nkv=700,
                                gqa=True)
     _run_check(w, q, k, v, idx, o)
+
+
+@pytest.mark.parametrize("G,dtype", [(24, "bf16"), (64, "f16"), (20, "f32")])
+@pytest.mark.parametrize("nsplit", [3, 5])
+def test_gqa_head_chunks_with_splits(G, dtype, nsplit):
+    # Head chunks and KV splits together: every (unit, chunk, split) partial
+    # lands in its own slot and the combine reads the group's G heads.
+    say(f"[edge] gqa G={G} {dtype} nsplit={nsplit}")
+    H_kv = 2
+    w, q, k, v, idx, o = _case(dtype=dtype, B=3, H=G * H_kv, H_kv=H_kv, top_k=2, Nkv=1500,
+                               gqa=True, seed=11)
+    _run_check(w, q, k, v, idx, o, nsplit=nsplit)
 
 
 def test_gqa_equals_mha_on_repeated_kv():

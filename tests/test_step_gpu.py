@@ -28,7 +28,23 @@ def _gen(seed):
     return g
 
 
-def _layers(cfg, n_layers, mlp, seed, seqlens_layer=None):
+def _to_pages(k, v, P, seed):
+    """The rows of k/v [B, H_kv, Nkv, d] scattered into pools of P-row pages
+    [num_pages, H_kv, P, d] in a seeded page order, and the block table."""
+    B, H_kv, Nkv, d = k.shape
+    npg = (Nkv + P - 1) // P
+    perm = torch.randperm(B * npg, generator=torch.Generator().manual_seed(seed)).reshape(B, npg)
+    kp = torch.zeros(B * npg, H_kv, P, d, dtype=k.dtype, device=DEV)
+    vp = torch.zeros_like(kp)
+    for b in range(B):
+        for j in range(npg):
+            r0, r1 = j * P, min((j + 1) * P, Nkv)
+            kp[perm[b, j], :, :r1 - r0] = k[b, :, r0:r1]
+            vp[perm[b, j], :, :r1 - r0] = v[b, :, r0:r1]
+    return kp, vp, perm.to(torch.int32).to(DEV)
+
+
+def _layers(cfg, n_layers, mlp, seed, seqlens_layer=None, paged=None):
     B, H, H_kv, d, Nkv = cfg["B"], cfg["H"], cfg["H_kv"], cfg["d"], cfg["Nkv"]
     dt = cfg["dtype"]
     nh = H_kv if cfg["gqa"] else H
@@ -44,6 +60,8 @@ def _layers(cfg, n_layers, mlp, seed, seqlens_layer=None):
             L["v"] = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
             L["seqlens"] = torch.randint(0, Nkv + 1, (B,), generator=g, device=DEV,
                                          dtype=torch.int32)
+        if paged is not None and l == paged[0]:
+            L["k"], L["v"], L["block_table"] = _to_pages(k, v, paged[1], seed=seed + l)
         if l > 0:
             L["router_x"] = torch.randn(B, cfg["router_d"], generator=g, device=DEV).to(dt)
             L["router_w"] = torch.randn(nh, cfg["router_d"], generator=g, device=DEV).to(dt)
@@ -77,8 +95,13 @@ def _eager(cfg, layers, mlp):
             r["index"], r["router_scores"] = idx, sc
         o = wl.sentinel_like(wl.Workload("s", B=B, H=cfg["H"], H_kv=cfg["H_kv"], d=cfg["d"],
                                          Nkv=cfg["Nkv"], top_k=1, dtype=cfg["dname"]), DEV)
-        r["o"] = fn(L["q"], L["k"], L["v"], idx, scale=cfg["scale"], out=o,
-                    seqlens=L.get("seqlens"))
+        if "block_table" in L:
+            r["o"] = sha.sha_decode_paged(L["q"], L["k"], L["v"], L["block_table"], idx,
+                                          cfg["Nkv"], gqa=cfg["gqa"], scale=cfg["scale"], out=o,
+                                          seqlens=L.get("seqlens"))
+        else:
+            r["o"] = fn(L["q"], L["k"], L["v"], idx, scale=cfg["scale"], out=o,
+                        seqlens=L.get("seqlens"))
         if mlp:
             md, mD, mk = mlp
             sel, n_sel = sha.mlp_union(L["mlp_rows"], mD)
@@ -129,27 +152,29 @@ def _refresh_inputs(layers, seed):
                                               device=DEV, dtype=torch.int32))
 
 
+# (config, MLP (d, D, k per row) or None, layer with per-row lengths, (paged
+# layer, page rows) or None)
 CASES = {
     "opt_mha_f16_mlp": (dict(B=8, H=8, H_kv=8, d=128, Nkv=300, top_k=3, gqa=False,
                              dtype=torch.float16, dname="f16", router_d=256),
-                        (256, 1024, 64), None),
+                        (256, 1024, 64), None, (2, 16)),
     "gqa_bf16_ragged": (dict(B=4, H=16, H_kv=4, d=128, Nkv=700, top_k=2, gqa=True,
                              dtype=torch.bfloat16, dname="bf16", router_d=512),
-                        None, 2),
+                        None, 2, (1, 64)),
     "mha_f32_d64": (dict(B=3, H=6, H_kv=6, d=64, Nkv=2100, top_k=2, gqa=False,
                          dtype=torch.float32, dname="f32", router_d=128),
-                    None, 1),
+                    None, 1, None),
 }
 
 
 @pytest.mark.parametrize("use_graph", [True, False])
 @pytest.mark.parametrize("case", list(CASES))
 def test_step_matches_per_call(case, use_graph):
-    cfg, mlp, sl_layer = CASES[case]
+    cfg, mlp, sl_layer, paged = CASES[case]
     cfg = dict(cfg, scale=1.0 / np.sqrt(cfg["d"]))
     say(f"[step] {case} graph={use_graph}")
     n_layers = 3
-    layers = _layers(cfg, n_layers, mlp, seed=17, seqlens_layer=sl_layer)
+    layers = _layers(cfg, n_layers, mlp, seed=17, seqlens_layer=sl_layer, paged=paged)
     md, mD, mk = mlp if mlp else (0, 0, 0)
     step = sha.DecodeStep(cfg["B"], cfg["H"], cfg["H_kv"], cfg["Nkv"], cfg["d"], cfg["top_k"],
                           cfg["dtype"], layers, gqa=cfg["gqa"], scale=cfg["scale"],
