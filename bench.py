@@ -90,6 +90,8 @@ def parse():
                         "dense) as one HIP graph and call by call")
     p.add_argument("--step-mlp", default=None, choices=list(wl.MLP_WORKLOADS),
                    help="MLP shape inside the decode step (its dtype follows the workload)")
+    p.add_argument("--router", default=None, choices=list(wl.WORKLOADS),
+                   help="time the attention router (scores + per-row top-k) of this layer shape")
     return p.parse_args()
 
 
@@ -322,6 +324,61 @@ def bench_mlp(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_router(args):
+    """Attention router of one layer on one GPU: scores = x W^T + b over the
+    token's hidden state (d_model = H * d) and the per-row top-k written as the
+    ascending index SHA reads.  The weights are read once per call; they are
+    small (~1 MB), so the call is launch- and latency-bound.  Timed twice: with
+    one weight matrix (warm: it stays in the caches between calls) and rotating
+    through enough copies (>= 512 MB) that every call reads its weights from
+    HBM, as a decode step that visits each layer once does."""
+    w = wl.WORKLOADS[args.router]
+    dev = torch.device("cuda:0")
+    dt = wl.DTYPES[w.dtype]
+    nh = w.H_kv if w.gqa else w.H
+    dm = w.H * w.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    x = torch.randn(w.B, dm, generator=g, device=dev).to(dt)
+    w0 = (torch.randn(nh, dm, generator=g, device=dev) / math.sqrt(dm)).to(dt)
+    bias = torch.randn(nh, generator=g, device=dev)
+    e = w0.element_size()
+    wbytes = nh * dm * e
+    copies = max(1, math.ceil((512 << 20) / wbytes))
+    ws = [w0] + [w0.roll(c, 0).contiguous() for c in range(1, copies)]
+    idx = torch.empty(w.B, w.top_k, dtype=torch.int32, device=dev)
+    sc = torch.empty(w.B, nh, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def cold(i):
+        sha.router_topk(x, ws[i % copies], w.top_k, bias=bias, index=idx, scores=sc, stream=stream)
+
+    def warm(i):
+        sha.router_topk(x, w0, w.top_k, bias=bias, index=idx, scores=sc, stream=stream)
+
+    ms, ev = time_calls(cold, args.steps, args.warmup, stream)
+    wms, wev = time_calls(warm, args.steps, args.warmup, stream)
+    nbytes = wbytes + w.B * dm * e + w.B * nh * 4 + w.B * w.top_k * 4
+    ev_us = float(np.mean(ev)) * 1e3
+    out = {"metric": f"attention router µs/call (scores + per-row top-k), {w.name}",
+           "value": round(ms * 1e3, 2), "unit": "us", "higher_is_better": False,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
+           "data": "synthetic: seeded N(0,1) hidden states, N(0, 1/d_model) router weights, "
+                   "N(0,1) bias",
+           "config": {"workload": w.name, "B": w.B, "d_model": dm, "heads": nh, "top_k": w.top_k,
+                      "gqa": w.gqa, "weight_bytes": wbytes, "weight_copies_rotated": copies},
+           "roofline": {"bound": "latency", "achieved": round(nbytes / (ev_us / 1e6) / 1e9, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(nbytes / (ev_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "bytes_per_call": nbytes, "launch_avg_us": round(ev_us, 2),
+                        "note": "event span covers the scores and top-k kernels; at "
+                                "8 TB/s the bytes alone would take "
+                                f"{nbytes / HBM_PEAK_GBS / 1e3:.2f} us"},
+           "warm_weights": {"us_per_call": round(wms * 1e3, 2),
+                            "launch_avg_us": round(float(np.mean(wev)) * 1e3, 2)}}
+    print(json.dumps(out), flush=True)
+
+
 def to_pages(w, ks, vs, page, dev):
     """Move each K/V copy into a pool of `page`-row pages [num_pages, page, H_kv, d]
     placed in a seeded random page order; returns [num_pages, H_kv, page, d]
@@ -401,12 +458,6 @@ def bench_step(args):
 
 def main():
     args = parse()
-    if args.decode_step:
-        bench_step(args)
-        return
-    if args.mlp:
-        bench_mlp(args)
-        return
     if args.summarize_traffic:
         summarize_traffic(args)
         return
@@ -415,6 +466,15 @@ def main():
               "library runs each layer call on a single MI355X; --gpus must be 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.decode_step:
+        bench_step(args)
+        return
+    if args.mlp:
+        bench_mlp(args)
+        return
+    if args.router:
+        bench_router(args)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)

@@ -11,10 +11,13 @@ BENCH = os.path.join(ROOT, "bench.py")
 
 
 def test_more_than_one_gpu_is_refused():
-    r = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True,
-                       timeout=300)
-    assert r.returncode == 2
-    assert "one GPU" in r.stderr
+    # Every mode (decode, MLP, router, decode step) measures one GPU.
+    for extra in ([], ["--mlp", "opt66b_mlp_bf16"], ["--router", "opt66b_f16"],
+                  ["--decode-step", "2"]):
+        r = subprocess.run([sys.executable, BENCH, "--gpus", "2"] + extra, capture_output=True,
+                           text=True, timeout=300)
+        assert r.returncode == 2, extra
+        assert "one GPU" in r.stderr
 
 
 def _write_counters(path, rows):
