@@ -611,6 +611,12 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
       !aligned(sel, 4) || !aligned(n_sel, 4))
     return SHA_ERR_MISALIGNED;
   const MlpPlan p = mlp_plan(B, d, n_max, 0);
+  // Both products launch 1-D grids: their workgroup counts must fit one
+  // grid dimension (and an int in the kernels).
+  const long long btiles = p.b_pad / 64;
+  if (static_cast<long long>(p.n_pad / sha::kMlpUpNeurons) * p.up_splits * btiles > 0x7FFFFFFFLL ||
+      static_cast<long long>(d / 256) * p.dn_splits * btiles > 0x7FFFFFFFLL)
+    return SHA_ERR_INVALID_ARG;
   const size_t need = p.h_bytes + p.up_bytes + p.dn_bytes;
   if (!workspace || workspace_bytes < need) return SHA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;

@@ -398,6 +398,7 @@ __global__ __launch_bounds__(256) void sha_mlp_up_finalize_kernel(MlpArgs a) {
 // ---------------------------------------------------------------------------
 // down projection: y = H W2t[S]
 // ---------------------------------------------------------------------------
+constexpr int kXcds = 8;                    // accelerator dies (XCDs) of MI355X
 constexpr int kDnKc = 64;                   // neurons per LDS chunk (2 MFMA K steps)
 constexpr int kDnCols = 256;                // output columns per workgroup
 constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 B: conflict-free transposed reads
@@ -411,9 +412,20 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
   __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
   const int n_sel = sel_count(a);
-  const int col0 = blockIdx.x * kDnCols;
-  const int split = blockIdx.y;
-  const int b0 = blockIdx.z * 64;
+  // Workgroup -> (column block, neuron split, batch tile), XCD-aware.  The
+  // dispatcher deals workgroups to the 8 XCDs in turn (id mod 8); each XCD
+  // is given a contiguous run of the split-major item list instead, so the
+  // workgroups on one XCD share a few neuron splits and the H slices those
+  // read stay in that XCD's L2 (with the plain order every XCD would read
+  // all of H, more than its L2 holds).
+  const int ncol = a.d / kDnCols;
+  const int nitems = static_cast<int>(gridDim.x);  // ncol * dn_splits * batch tiles
+  const int L = blockIdx.x, xcd = L % kXcds, slot = L / kXcds;
+  const int q8 = nitems / kXcds, r8 = nitems % kXcds;
+  const int item = xcd * q8 + min(xcd, r8) + slot;  // a bijection of [0, nitems)
+  const int col0 = (item % ncol) * kDnCols;
+  const int split = (item / ncol) % a.dn_splits;
+  const int b0 = (item / (ncol * a.dn_splits)) * 64;
   // This split's neuron range (whole MFMA K steps).
   const int per = ((n_sel + a.dn_splits - 1) / a.dn_splits + 31) / 32 * 32;
   const int nbeg = min(split * per, n_sel);
@@ -594,7 +606,10 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((sha_mlp_up_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((sha_mlp_down_kernel<DT>), dim3(a.d / kDnCols, a.dn_splits, btiles),
+  // 1-D over (column block, split, batch tile): the kernel maps the ids
+  // onto XCDs itself.
+  hipLaunchKernelGGL((sha_mlp_down_kernel<DT>),
+                     dim3(static_cast<unsigned>((a.d / kDnCols) * a.dn_splits) * btiles),
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dn_splits > 1) {

@@ -163,6 +163,10 @@ def test_mlp_host_validation():
     assert mlp(sel=None) == 1
     assert mlp(x=P + 8) == 3
     assert mlp(ws=None) == 4
+    # grids past 2^31 - 1 workgroups are refused before any launch: 65535
+    # batch tiles x 32769 up-projection neuron tiles of a 256-wide MLP
+    assert mlp(B=65535 * 64, d=256, D=32769 * 128, n_max=32769 * 128) == 1
+    assert mlp(B=65535 * 64, d=256, D=32768 * 128, n_max=32768 * 128) == 4   # fits: workspace next
     need = L.sha_selective_mlp_workspace_bytes(4, 256, 1000, 64, 256)
     assert need > 0 and mlp(wsb=need - 1) == 4
 
