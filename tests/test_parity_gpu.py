@@ -54,3 +54,27 @@ def test_full_size_sampled(name):
     say(f"   max_err={err:.3e}")
     del q, k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("gqa,dtype", [(False, "f16"), (True, "bf16")])
+@pytest.mark.parametrize("nsplit", [0, 64])
+def test_long_context(gqa, dtype, nsplit):
+    """A 128 K-key cache with few units: the planner splits up to its cap
+    (64 splits of 2048 keys for the head kernel), every active slot is
+    checked against the oracle, and inactive slots keep their bits."""
+    if gqa:
+        w = wl.Workload("long", B=2, H=16, H_kv=2, d=128, Nkv=131072, top_k=1, dtype=dtype,
+                        gqa=True, seed=21)
+    else:
+        w = wl.Workload("long", B=2, H=4, H_kv=4, d=128, Nkv=131072, top_k=2, dtype=dtype,
+                        seed=21)
+    say(f"[parity long] gqa={gqa} {dtype} Nkv={w.Nkv} nsplit={nsplit}")
+    q, k, v, idx, o = wl.make_workload(w, DEV)
+    before_bits = wl.raw_bits(o).clone()
+    run_gpu(w.gqa, q, k, v, idx, w.scale, o, nsplit=nsplit)
+    n_active = w.B * w.top_k * (w.H // w.H_kv if gqa else 1)
+    err = check_sampled(w.gqa, q, k, v, idx, w.scale, before_bits, o, TOL[w.dtype],
+                        n_samples=n_active, seed=w.seed)
+    say(f"   max_err={err:.3e}")
+    del q, k, v
+    torch.cuda.empty_cache()
