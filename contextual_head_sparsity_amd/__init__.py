@@ -7,15 +7,15 @@ error: there is no CPU fallback.
 """
 from . import workloads
 
-__all__ = ["workloads", "sha_decode", "sha_decode_gqa", "sha_decode_paged", "DecodeStep", "lib", "mlp_union",
-           "selective_mlp", "router_topk"]
+_BINDING_NAMES = ("sha_decode", "sha_decode_gqa", "sha_decode_paged", "KvLayout", "DecodeStep",
+                  "ShaError", "lib", "plan_nsplit", "workspace_bytes", "workspace_bytes_paged",
+                  "router_topk", "mlp_union", "selective_mlp", "selective_mlp_workspace_bytes")
+
+__all__ = ["workloads", *_BINDING_NAMES]
 
 
 def __getattr__(name):
-    if name in ("sha_decode", "sha_decode_gqa", "sha_decode_paged", "KvLayout", "lib",
-                "plan_nsplit", "workspace_bytes", "workspace_bytes_paged", "DecodeStep",
-                "ShaError", "mlp_union", "selective_mlp", "selective_mlp_workspace_bytes",
-                "router_topk"):
+    if name in _BINDING_NAMES:
         from . import _binding
         return getattr(_binding, name)
     raise AttributeError(name)
