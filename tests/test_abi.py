@@ -318,3 +318,26 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         bd.workspace_bytes(1, 4, 4, 64, 64, 1)
     with pytest.raises(ImportError):
         bd.selective_mlp_workspace_bytes(1, 256, 512, 64)
+
+
+@pytest.mark.parametrize("header", ["sha.h", "sha_probe.h"])
+def test_headers_compile_as_c(header, tmp_path):
+    """The boundary is a C ABI: each public header compiles as C11, and no
+    diagnostic (with -Wall -Wextra -pedantic) points into it."""
+    import shutil
+    import subprocess
+    cc = "/opt/rocm/llvm/bin/clang"
+    if not os.path.exists(cc):
+        cc = shutil.which("clang")
+    if cc is None:
+        pytest.skip("no clang to compile C with")
+    src = tmp_path / "use.c"
+    src.write_text(f'#include "{header}"\nint main(void) {{ return 0; }}\n')
+    r = subprocess.run([cc, "-x", "c", "-std=c11", "-Wall", "-Wextra", "-pedantic",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                        "-D__HIP_PLATFORM_AMD__", "-fsyntax-only", str(src)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    ours = [ln for ln in r.stderr.splitlines()
+            if os.path.join("include", header) in ln and ("warning" in ln or "error" in ln)]
+    assert not ours, ours
