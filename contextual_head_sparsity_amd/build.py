@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsha.so")
 PROBE_LIB = os.path.join(PKG, "libsha_probe.so")
+EXAMPLE = os.path.join(PKG, "examples", "decode_c")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU ops are disabled for all device code; hipcc's host pass
@@ -61,6 +63,15 @@ def build(verbose: bool = True) -> str:
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
           os.path.join(PKG, "probe", "sha_probe.hip"), "-o", tmp])
     os.replace(tmp, PROBE_LIB)
+    # The plain-C example of the ABI, linked against the library just built.
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler for the C-ABI example")
+    tmp = EXAMPLE + ".tmp"
+    _run([cc, "-std=c11", "-O2", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{ROCM}/include",
+          "-D__HIP_PLATFORM_AMD__", EXAMPLE + ".c", f"-L{PKG}", "-lsha", f"-L{ROCM}/lib",
+          "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{ROCM}/lib", "-o", tmp])
+    os.replace(tmp, EXAMPLE)
     return LIB
 
 
