@@ -160,10 +160,15 @@ def read_probe(dev, nbytes: int = 1 << 31):
             "kernel": "sha_probe_read_kernel (libsha_probe.so)"}
 
 
-def cpu_baseline(w, q, k, v, idx, budget_s: float):
+ORACLE_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}   # max abs error, N(0, 1) inputs
+
+
+def cpu_baseline(w, q, k, v, idx, budget_s: float, o_gpu=None):
     """The fp64 oracle on the host cores: whole layer calls of this workload
     (every active unit, inputs copied to host memory first), repeated until
-    about budget_s of CPU work has been timed."""
+    about budget_s of CPU work has been timed.  With o_gpu (the HIP path's
+    output for the same inputs) the first pass's results are also compared
+    with it slot by slot."""
     from oracle import sha_units_ref
     try:
         from threadpoolctl import threadpool_info
@@ -180,12 +185,18 @@ def cpu_baseline(w, q, k, v, idx, budget_s: float):
         rows.append((torch.stack([q[b, h, 0] for h, _ in units]).cpu(),
                      torch.stack([k[b, g] for _, g in units]).cpu(),
                      torch.stack([v[b, g] for _, g in units]).cpu()))
-    spent, passes = 0.0, 0
+    spent, passes, err = 0.0, 0, None
     while spent < budget_s and passes < 100:
         t0 = time.perf_counter()
-        for qs, ks, vs in rows:
-            sha_units_ref(qs, ks, vs, w.scale)
+        refs = [sha_units_ref(qs, ks, vs, w.scale) for qs, ks, vs in rows]
         spent += time.perf_counter() - t0
+        if passes == 0 and o_gpu is not None:
+            err = 0.0
+            for b, ref in enumerate(refs):
+                heads = [int(e) for e in idx_cpu[b]]
+                hs = ([h for g in heads for h in range(g * G, g * G + G)] if w.gqa else heads)
+                got = torch.stack([o_gpu[b, h, 0] for h in hs]).cpu().to(torch.float64).numpy()
+                err = max(err, float(np.max(np.abs(got - ref))))
         passes += 1
     per_call = spent / passes
     try:
@@ -198,7 +209,9 @@ def cpu_baseline(w, q, k, v, idx, budget_s: float):
             "affinity_cores": affinity, "blas_threads": threads,
             "sample": f"{passes} full layer call(s) of {w.name} ({w.units} units, "
                       f"{w.active_kv_bytes / 1e6:.0f} MB active K/V each), fp64 numpy oracle, "
-                      f"{spent:.1f} s timed, {per_call * 1e6:.0f} us per layer call"}
+                      f"{spent:.1f} s timed, {per_call * 1e6:.0f} us per layer call",
+            "max_abs_err_vs_gpu": err, "tol": ORACLE_TOL[w.dtype],
+            "within_tol": None if err is None else bool(err <= ORACLE_TOL[w.dtype])}
 
 
 def traffic_path(workload: str) -> str:
@@ -515,12 +528,12 @@ def main():
     elif layout != "contig":
         raise SystemExit(f"unknown --kv-layout {layout}")
 
-    def call(i, index=idx):
+    def call(i, index=idx, out=o):
         if page:
             sha.sha_decode_paged(q, ks[i % copies], vs[i % copies], bt, index, w.Nkv, gqa=w.gqa,
-                                 scale=w.scale, out=o, nsplit=nsplit, workspace=ws, stream=stream)
+                                 scale=w.scale, out=out, nsplit=nsplit, workspace=ws, stream=stream)
         else:
-            fn(q, ks[i % copies], vs[i % copies], index, scale=w.scale, out=o, nsplit=nsplit,
+            fn(q, ks[i % copies], vs[i % copies], index, scale=w.scale, out=out, nsplit=nsplit,
                workspace=ws, stream=stream)
 
     ms, ev = time_calls(call, args.steps, args.warmup, stream)
@@ -583,11 +596,31 @@ def main():
                               if nsplit > 1 else "event span covers the one decode kernel")},
         "all_heads": dense,
     }
+    # One more call, outside the timed region, into a fresh sentinel-filled
+    # output on the first K/V copy: unselected slots must keep their bits and
+    # selected ones must be finite (the oracle leg below also compares them).
+    o_chk = wl.sentinel_like(w, dev)
+    call(0, out=o_chk)
+    torch.cuda.synchronize()
+    idx_cpu = idx.cpu().numpy()
+    G = w.H // w.H_kv
+    sel = torch.zeros(w.B, w.H, dtype=torch.bool)
+    for b in range(w.B):
+        for e in idx_cpu[b]:
+            if w.gqa and 0 <= e < w.H_kv:
+                sel[b, e * G:(e + 1) * G] = True
+            elif not w.gqa and 0 <= e < w.H:
+                sel[b, e] = True
+    sel = sel.to(dev)
+    out["check"] = {"active_slots": int(sel.sum()),
+                    "unselected_bits_untouched": bool(torch.equal(
+                        wl.raw_bits(o_chk)[~sel], wl.raw_bits(wl.sentinel_like(w, dev))[~sel])),
+                    "selected_finite": bool(torch.isfinite(o_chk[sel]).all())}
     probe = read_probe(dev) if not args.no_probe else None
     out["read_probe"] = probe
     out["pct_of_read_probe"] = round(100 * value / probe["GBps"], 2) if probe else None
     if not args.no_cpu_baseline and layout == "contig":
-        out["cpu_baseline"] = cpu_baseline(w, q, ks[0], vs[0], idx, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q, ks[0], vs[0], idx, args.cpu_seconds, o_gpu=o_chk)
     print(json.dumps(out), flush=True)
 
 
