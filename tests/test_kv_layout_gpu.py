@@ -239,3 +239,20 @@ def test_full_size_llama70b_paged():
     torch.cuda.synchronize()
     err = _sampled_ragged(w, q, k, v, idx, lens, bits, o, 48, 2)
     say(f"   max_err={err:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("gqa", [False, True])
+def test_d64_strided_and_paged(dtype, gqa):
+    """Head dimension 64 (half-width rows) through the strided and paged
+    layouts, with ragged lengths, split and unsplit."""
+    say(f"[kv] d=64 dtype={dtype} gqa={gqa}")
+    w, q, k, v, idx, o = _case(dtype, gqa, B=4, Nkv=900, d=64, seed=13)
+    lens = np.array([900, 1, 450, 0], dtype=np.int32)
+    lens_d = torch.from_numpy(lens).to(DEV)
+    for nsplit in (1, 3):
+        got = _call(w, q, _bnhd(k), _bnhd(v), idx, o, nsplit=nsplit, seqlens=lens_d)
+        _check(w, q, k, v, idx, o, got, seqlens=lens)
+        kp, vp, bt = _paged(w, k, v, 32, "nphd", seed=3)
+        got = _call_paged(w, q, kp, vp, bt, idx, o, nsplit=nsplit, seqlens=lens_d)
+        _check(w, q, k, v, idx, o, got, seqlens=lens)
