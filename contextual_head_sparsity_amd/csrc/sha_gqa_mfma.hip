@@ -133,8 +133,8 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   constexpr int ROWB = D * 2;                // bytes per key row
   constexpr int PITCH = ROWB + 32;           // LDS row pitch: conflict-free transposed reads
   constexpr int VBUF = kTileKeys * PITCH;    // LDS bytes per wave (V tile, later the partial O)
-  constexpr int VLD = kTileKeys * ROWB / 1024;  // 128-bit V loads per lane per tile
-  constexpr int LPRW = ROWB / 16;            // lanes per V row in a load
+  constexpr int VLD = kTileKeys * ROWB / 1024;  // 128-bit K (and V) loads per lane per tile
+  constexpr int LPRW = ROWB / 16;            // lanes per K/V row in a load
   constexpr int PO = D + 4;                  // partial-O row pitch (floats): conflict-free writes
   static_assert(kCols * PO * 4 + kCols * 2 * 4 <= VBUF, "partial O must fit the V buffer");
   constexpr int KPITCH = ROWB + 16;          // K rows: conflict-free 128-bit operand reads
