@@ -656,6 +656,8 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
   if (dtype != SHA_F32 && dtype != SHA_F16 && dtype != SHA_BF16) return SHA_ERR_UNSUPPORTED;
   if (H > sha::kRouterMaxH) return SHA_ERR_UNSUPPORTED;
   if (d % (dtype == SHA_F32 ? 4 : 8) != 0) return SHA_ERR_UNSUPPORTED;
+  // The scores grid has up to B * ceil(H / 2) workgroups of 512 threads.
+  if (static_cast<long long>(B) * ((H + 1) / 2) > (1LL << 22)) return SHA_ERR_INVALID_ARG;
   if (B == 0) return SHA_OK;
   if (!x || !w || !scores || (top_k > 0 && !batch_head_index)) return SHA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scores, 4) ||
@@ -663,7 +665,7 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
     return SHA_ERR_MISALIGNED;
   sha::RouterArgs a{x, w, bias, scores, batch_head_index, B, d, H, top_k};
   (void)hipGetLastError();
-  const hipError_t e = sha::launch_router(a, dtype, stream);
+  const hipError_t e = sha::launch_router(a, dtype, device_cus(0), stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;
     return SHA_ERR_HIP;

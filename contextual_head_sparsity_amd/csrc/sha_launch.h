@@ -50,7 +50,8 @@ struct RouterArgs {
   int B, d, H, top_k;
 };
 
-hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t stream);
+// num_cus: the device's compute units (picks the heads per scores workgroup).
+hipError_t launch_router(const RouterArgs& a, int dtype, int num_cus, hipStream_t stream);
 
 // Records the hipError_t that sha_last_hip_error() reports on this thread.
 void set_last_hip_error(int e);

@@ -9,11 +9,12 @@
 // (batch_head_index [B, top_k], ascending), so router -> attention needs no
 // host synchronisation.
 //
-//   scores kernel: one workgroup per (batch row, 8 consecutive heads); its
-//                  four waves take a quarter of the hidden dimension each in
-//                  16-byte pieces (v_dot2 for 16-bit inputs, fp32
-//                  accumulation), DPP + shuffle wave sums, the quarters
-//                  added in a fixed order.
+//   scores kernel: one workgroup per (batch row, 4 consecutive heads; 2 when
+//                  the grid would not fill the CUs); its eight waves take
+//                  64-piece blocks of the hidden dimension in turn, 16-byte
+//                  pieces (v_dot2 for 16-bit inputs, fp32 accumulation), DPP
+//                  + shuffle wave sums, the waves' partials added in a fixed
+//                  order.
 //   top-k kernel : one wave per batch row; each head's rank in the (score
 //                  descending, index ascending) order is counted against the
 //                  row staged in LDS (NaN ranked as -inf) and the heads of
@@ -37,66 +38,63 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-constexpr int kScoreHeads = 8;   // heads per scores workgroup
-constexpr int kScoreWaves = 4;   // the hidden dimension is cut in 4 contiguous quarters
-constexpr int kScoreUnroll = 4;  // 16-byte pieces per lane in flight per head (and of x)
+constexpr int kScoreWaves = 8;  // waves per scores workgroup
 
-// One workgroup per (batch row, 8 consecutive heads); wave w dots the w-th
-// quarter of the hidden dimension, kScoreUnroll pieces of x and of each head's
-// row in flight per lane; the four quarters are added in a fixed order.
-template <int DT>
+// One workgroup per (batch row, HEADS consecutive heads).  The hidden
+// dimension is cut into blocks of 64 16-byte pieces and wave w takes blocks
+// w, w + 8, ...: a lane dots its piece of the row against the same piece of
+// each head.  Whole blocks keep the waves' shares within one block of each
+// other and spend no load on clamped duplicates except in a ragged last
+// block.  Sums: per lane in block order, a wave sum, then the 8 waves'
+// partials added in a fixed order, so the result does not depend on timing.
+template <int DT, int HEADS>
 __global__ __launch_bounds__(kScoreWaves * 64) void sha_router_scores_kernel(RouterArgs a) {
   using E = Elem<DT>;
   constexpr int VEC = E::VEC;
   constexpr int ES = 16 / VEC;
-  __shared__ float part[kScoreWaves][kScoreHeads];
-  const int nhg = (a.H + kScoreHeads - 1) / kScoreHeads;
+  __shared__ float part[kScoreWaves][HEADS];
+  const int nhg = (a.H + HEADS - 1) / HEADS;
   const int b = blockIdx.x / nhg, hg = blockIdx.x % nhg;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Quarter of the hidden dimension, in whole 16-byte pieces.
   const int pieces = a.d / VEC;
-  const int q0 = (pieces * wave) / kScoreWaves, q1 = (pieces * (wave + 1)) / kScoreWaves;
+  const int nblk = (pieces + 63) / 64;
   const char* xr = static_cast<const char*>(a.x) + static_cast<size_t>(b) * a.d * ES;
-  const char* wb = static_cast<const char*>(a.w);
-  float acc[kScoreHeads];
+  const char* wr[HEADS];
+  // Heads past H read head H - 1 and are never stored.
 #pragma unroll
-  for (int j = 0; j < kScoreHeads; ++j) acc[j] = 0.f;
-  // Loads are unconditional (clamped to the quarter's last piece and to head
-  // H - 1) so that all of them are in flight together; pieces past the
-  // quarter add nothing and heads past H are never stored.
-  for (int p0 = q0 + lane; p0 < q1; p0 += 64 * kScoreUnroll) {
-    uint4 xv[kScoreUnroll], wv[kScoreUnroll][kScoreHeads];
+  for (int j = 0; j < HEADS; ++j)
+    wr[j] = static_cast<const char*>(a.w) +
+            static_cast<size_t>(min(hg * HEADS + j, a.H - 1)) * a.d * ES;
+  float acc[HEADS];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int p = min(p0 + 64 * u, q1 - 1);
-      xv[u] = ld16(xr + static_cast<size_t>(p) * 16);
+  for (int j = 0; j < HEADS; ++j) acc[j] = 0.f;
+  for (int blk = wave; blk < nblk; blk += kScoreWaves) {
+    const int piece = blk * 64 + lane;
+    // Unconditional loads (a ragged last block clamps to the last piece),
+    // all in flight together.
+    const size_t p = static_cast<size_t>(min(piece, pieces - 1)) * 16;
+    const uint4 xv = ld16(xr + p);
+    uint4 wv[HEADS];
 #pragma unroll
-      for (int j = 0; j < kScoreHeads; ++j) {
-        const int h = min(hg * kScoreHeads + j, a.H - 1);
-        wv[u][j] = ld16(wb + (static_cast<size_t>(h) * a.d * ES) + static_cast<size_t>(p) * 16);
-      }
-    }
+    for (int j = 0; j < HEADS; ++j) wv[j] = ld16(wr[j] + p);
     // Keep every load above the first use: the scheduler would otherwise
     // interleave them with the dot products and wait on each in turn.
     __builtin_amdgcn_sched_barrier(0);
+    const bool ok = piece < pieces;
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const bool ok = p0 + 64 * u < q1;
-#pragma unroll
-      for (int j = 0; j < kScoreHeads; ++j) {
-        const float t = E::dot(xv[u], wv[u][j]);
-        acc[j] += ok ? t : 0.f;
-      }
+    for (int j = 0; j < HEADS; ++j) {
+      const float t = E::dot(xv, wv[j]);
+      acc[j] += ok ? t : 0.f;
     }
   }
 #pragma unroll
-  for (int j = 0; j < kScoreHeads; ++j) {
+  for (int j = 0; j < HEADS; ++j) {
     const float s = wave_sum(acc[j]);
     if (lane == 0) part[wave][j] = s;
   }
   __syncthreads();
-  if (threadIdx.x < kScoreHeads) {
-    const int j = threadIdx.x, h = hg * kScoreHeads + j;
+  if (threadIdx.x < HEADS) {
+    const int j = threadIdx.x, h = hg * HEADS + j;
     if (h < a.H) {
       float s = 0.f;
 #pragma unroll
@@ -172,11 +170,21 @@ hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DT>
-hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
-  const long long wgs = static_cast<long long>(a.B) * ((a.H + kScoreHeads - 1) / kScoreHeads);
-  hipLaunchKernelGGL((sha_router_scores_kernel<DT>), dim3(static_cast<unsigned>(wgs)),
+template <int DT, int HEADS>
+void launch_scores(const RouterArgs& a, hipStream_t st) {
+  const long long wgs = static_cast<long long>(a.B) * ((a.H + HEADS - 1) / HEADS);
+  hipLaunchKernelGGL((sha_router_scores_kernel<DT, HEADS>), dim3(static_cast<unsigned>(wgs)),
                      dim3(kScoreWaves * 64), 0, st, a);
+}
+
+template <int DT>
+hipError_t launch_router_t(const RouterArgs& a, int num_cus, hipStream_t st) {
+  // 4 heads per workgroup; 2 when that leaves CUs idle (small batches or
+  // few heads), trading more reads of the row for more workgroups.
+  if (static_cast<long long>(a.B) * ((a.H + 3) / 4) < num_cus)
+    launch_scores<DT, 2>(a, st);
+  else
+    launch_scores<DT, 4>(a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.top_k == 0) return e;
   const int slots = (a.H + 63) / 64;
@@ -189,11 +197,11 @@ hipError_t launch_router_t(const RouterArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_router(const RouterArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_router(const RouterArgs& a, int dtype, int num_cus, hipStream_t st) {
   switch (dtype) {
-    case kF32: return launch_router_t<kF32>(a, st);
-    case kF16: return launch_router_t<kF16>(a, st);
-    default: return launch_router_t<kBF16>(a, st);
+    case kF32: return launch_router_t<kF32>(a, num_cus, st);
+    case kF16: return launch_router_t<kF16>(a, num_cus, st);
+    default: return launch_router_t<kBF16>(a, num_cus, st);
   }
 }
 

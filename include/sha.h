@@ -248,7 +248,8 @@ size_t sha_workspace_bytes_kv(int B, int H, int H_kv, int Nkv, int d, int top_k,
  *   scores: [B, H] fp32 device output (always written);
  *   batch_head_index: [B, top_k] int32 device output (may be null if top_k = 0).
  * Limits: 1 <= H <= 1024, 0 <= top_k <= H, d a multiple of 8 (4 for f32),
- * else SHA_ERR_INVALID_ARG / SHA_ERR_UNSUPPORTED.  B == 0 is an empty call.
+ * else SHA_ERR_INVALID_ARG / SHA_ERR_UNSUPPORTED; B * ceil(H / 2) at most
+ * 2^22 (the scores grid), else SHA_ERR_INVALID_ARG.  B == 0 is an empty call.
  * x and w 16-byte aligned, the others 4-byte aligned (SHA_ERR_MISALIGNED).
  */
 sha_status sha_router_topk(const void* x, const void* w, const float* bias, int B, int d, int H,

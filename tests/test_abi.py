@@ -201,6 +201,9 @@ def test_router_host_validation():
     assert r(B=0, x=None, w=None, idx=None, sc=None) == 0
     assert r(sc=None) == 1 and r(idx=None) == 1
     assert r(x=P + 8) == 3 and r(idx=P + 2) == 3 and r(bias=P + 2) == 3
+    # the scores grid: B * ceil(H / 2) workgroups, at most 2^22
+    assert r(B=(1 << 22) // 36 + 1) == 1 and r(B=(1 << 22) // 36, x=None) == 1
+    assert r(B=1 << 22, H=1, k=1, x=None) == 1 and r(B=(1 << 22) + 1, H=1, k=1) == 1
 
 
 def _kv_layout(**kw):

@@ -60,11 +60,16 @@ def _check(x, w, b, k, idx_gpu, sc_gpu):
     return exact
 
 
+# The shapes take both heads-per-workgroup choices of the scores kernel (4,
+# and 2 when B * ceil(H / 4) is below the CU count), head counts that leave a
+# partial head group, hidden sizes whose last 64-piece block is ragged, and
+# more blocks than the workgroup has waves.
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("B,d,H,k", [(1, 64, 8, 3), (64, 9216, 72, 22), (16, 4096, 32, 16),
                                      (5, 8192, 8, 5), (3, 512, 1000, 300), (7, 256, 64, 64),
                                      (2, 128, 40, 0), (4, 256, 200, 50), (3, 320, 300, 100),
-                                     (2, 8, 1024, 1000)])
+                                     (2, 8, 1024, 1000), (50, 1000, 37, 9), (9, 2056, 13, 4),
+                                     (3, 33000, 5, 2)])
 def test_router_matches_oracle(dtype, B, d, H, k):
     say(f"[router] {dtype} B={B} d={d} H={H} k={k}")
     x, w, b = _inputs(B, d, H, dtype, seed=B * 7 + H)
