@@ -1,5 +1,7 @@
 """Shared helpers for the GPU parity tests: run the HIP path through the C ABI
 and compare with the fp64 oracle element by element."""
+import math
+
 import numpy as np
 import torch
 
@@ -79,3 +81,48 @@ def check_sampled(gqa, q, k, v, idx, scale, o_before_bits, o_after, tol, n_sampl
     err = float(np.max(np.abs(got - ref)))
     assert err <= tol, f"max abs error {err:.3e} > {tol} on sampled slots"
     return err
+
+
+def bnhd(t):
+    """The same values stored as [B, Nkv, H_kv, d], viewed as [B, H_kv, Nkv, d]."""
+    return t.to(DEV).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+
+
+def ragged(w, k, v, lens):
+    """Rows past each row's length are NaN, so any read of them would show."""
+    k, v = k.clone(), v.clone()
+    for b, n in enumerate(lens):
+        n = max(0, min(int(n), w.Nkv))
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    return k, v
+
+
+def paged(w, k, v, P, pool="nphd", seed=0, extra=3):
+    """Scatter the rows of k/v into a page pool in a seeded page order.
+
+    Unused pages and the tail of each row's last page are NaN, and the block
+    table entries past a row's pages hold a huge id, so a read outside a
+    row's keys would show up as NaN."""
+    B, H_kv, Nkv, d = k.shape
+    npg = math.ceil(Nkv / P)
+    num_pages = B * npg + extra
+    perm = np.random.default_rng(seed).permutation(num_pages)[:B * npg].reshape(B, npg)
+    shape = (num_pages, P, H_kv, d) if pool == "nphd" else (num_pages, H_kv, P, d)
+    kp = torch.full(shape, float("nan"), dtype=k.dtype)
+    vp = torch.full(shape, float("nan"), dtype=v.dtype)
+    for b in range(B):
+        for j in range(npg):
+            r0, r1 = j * P, min((j + 1) * P, Nkv)
+            if pool == "nphd":
+                kp[perm[b, j], :r1 - r0] = k[b, :, r0:r1].transpose(0, 1)
+                vp[perm[b, j], :r1 - r0] = v[b, :, r0:r1].transpose(0, 1)
+            else:
+                kp[perm[b, j], :, :r1 - r0] = k[b, :, r0:r1]
+                vp[perm[b, j], :, :r1 - r0] = v[b, :, r0:r1]
+    bt = np.full((B, npg + 2), 10 ** 9, dtype=np.int32)
+    bt[:, :npg] = perm
+    kd, vd = kp.to(DEV), vp.to(DEV)
+    if pool == "nphd":
+        kd, vd = kd.permute(0, 2, 1, 3), vd.permute(0, 2, 1, 3)
+    return kd, vd, torch.from_numpy(bt).to(DEV)

@@ -4,8 +4,6 @@ each against the fp64 oracle with the same lengths, plus exact properties
 (bitwise equality with the contiguous call where the arithmetic order is the
 same, untouched inactive slots, no read past a row's length or outside its
 pages)."""
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -17,7 +15,8 @@ from oracle import sha_decode_gqa_ref, sha_decode_ref, sha_units_ref
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_util import DEV, TOL, say, written_mask
+    from gpu_util import DEV, TOL, bnhd as _bnhd, paged as _paged, ragged as _ragged, say, \
+        written_mask
 
 
 def _case(dtype, gqa, B=4, Nkv=300, d=128, seed=11):
@@ -51,11 +50,6 @@ def _call(w, q, k, v, idx, o, **kw):
     return out
 
 
-def _bnhd(t):
-    """The same values stored as [B, Nkv, H_kv, d], viewed as [B, H_kv, Nkv, d]."""
-    return t.to(DEV).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-
-
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("gqa", [False, True])
 @pytest.mark.parametrize("nsplit", [1, 3, 0])
@@ -70,16 +64,6 @@ def test_strided_bnhd_cache(dtype, gqa, nsplit):
     # K and V with different layouts in one call.
     mixed = _call(w, q, _bnhd(k), v.to(DEV), idx, o, nsplit=nsplit)
     assert torch.equal(wl.raw_bits(mixed), wl.raw_bits(ref))
-
-
-def _ragged(w, k, v, lens):
-    """Rows past each row's length are NaN, so any read of them would show."""
-    k, v = k.clone(), v.clone()
-    for b, n in enumerate(lens):
-        n = max(0, min(int(n), w.Nkv))
-        k[b, :, n:] = float("nan")
-        v[b, :, n:] = float("nan")
-    return k, v
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -100,36 +84,6 @@ def test_ragged_seqlens(dtype, gqa, nsplit):
     # Strided and ragged together.
     got2 = _call(w, q, _bnhd(k), _bnhd(v), idx, o, nsplit=nsplit, seqlens=sl)
     assert torch.equal(wl.raw_bits(got2), wl.raw_bits(got))
-
-
-def _paged(w, k, v, P, pool="nphd", seed=0, extra=3):
-    """Scatter the rows of k/v into a page pool in a seeded page order.
-
-    Unused pages and the tail of each row's last page are NaN, and the block
-    table entries past a row's pages hold a huge id, so a read outside a
-    row's keys would show up as NaN."""
-    B, H_kv, Nkv, d = k.shape
-    npg = math.ceil(Nkv / P)
-    num_pages = B * npg + extra
-    perm = np.random.default_rng(seed).permutation(num_pages)[:B * npg].reshape(B, npg)
-    shape = (num_pages, P, H_kv, d) if pool == "nphd" else (num_pages, H_kv, P, d)
-    kp = torch.full(shape, float("nan"), dtype=k.dtype)
-    vp = torch.full(shape, float("nan"), dtype=v.dtype)
-    for b in range(B):
-        for j in range(npg):
-            r0, r1 = j * P, min((j + 1) * P, Nkv)
-            if pool == "nphd":
-                kp[perm[b, j], :r1 - r0] = k[b, :, r0:r1].transpose(0, 1)
-                vp[perm[b, j], :r1 - r0] = v[b, :, r0:r1].transpose(0, 1)
-            else:
-                kp[perm[b, j], :, :r1 - r0] = k[b, :, r0:r1]
-                vp[perm[b, j], :, :r1 - r0] = v[b, :, r0:r1]
-    bt = np.full((B, npg + 2), 10 ** 9, dtype=np.int32)
-    bt[:, :npg] = perm
-    kd, vd = kp.to(DEV), vp.to(DEV)
-    if pool == "nphd":
-        kd, vd = kd.permute(0, 2, 1, 3), vd.permute(0, 2, 1, 3)
-    return kd, vd, torch.from_numpy(bt).to(DEV)
 
 
 def _call_paged(w, q, kp, vp, bt, idx, o, **kw):

@@ -1,0 +1,96 @@
+"""Seeded sweep of decode calls that mix the features the other GPU tests
+take one at a time: head-indexed calls with shared KV heads and group calls
+with G from 1 to 32, d = 64 / 128, all three element types, cache lengths
+from 1 to 3000 keys (ragged per row or not), contiguous, [B, Nkv, H_kv, d]
+strided and paged caches, library-planned and forced split counts, and index
+rows holding padding (-1, out of range) and repeated entries.  Each call is
+compared with the fp64 oracle on the same inputs (active slots within the
+dtype tolerance, inactive slots bit-identical to their prefill) and run twice
+for bitwise determinism.  Rows past a row's length are NaN in the cache, so
+a read beyond it shows."""
+import numpy as np
+import pytest
+import torch
+
+import contextual_head_sparsity_amd as sha
+from contextual_head_sparsity_amd import workloads as wl
+from oracle import sha_decode_gqa_ref, sha_decode_ref
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_util import DEV, TOL, bnhd, paged, ragged, say
+
+N_CASES = 48
+
+
+def _case(i):
+    rng = np.random.default_rng(9100 + i)
+    dtype = ("f32", "f16", "bf16")[int(rng.integers(3))]
+    gqa = bool(rng.integers(2))
+    d = (64, 128)[int(rng.integers(2))]
+    B = int(rng.integers(1, 7))
+    Nkv = max(1, int(np.exp(rng.uniform(0.0, np.log(3000.0)))))
+    if gqa:
+        H_kv = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 17, 32]))
+        H, n_sel = H_kv * G, H_kv
+    else:
+        H = int(rng.integers(1, 25))
+        H_kv = int(rng.choice([x for x in (1, 2, 3, 4, H) if H % x == 0]))
+        n_sel = H
+    top_k = int(rng.integers(1, n_sel + 1))
+    idx = np.stack([rng.permutation(n_sel)[:top_k] for _ in range(B)]).astype(np.int32)
+    if top_k >= 2 and rng.integers(2):        # padding: -1 and an id past the range
+        idx[0, -1] = -1
+        idx[-1, 0] = n_sel
+    if top_k >= 3 and rng.integers(2):        # a repeated entry
+        idx[B // 2, 1] = idx[B // 2, 2]
+    layout = ("contig", "bnhd", "paged16", "paged64")[int(rng.integers(4))]
+    lens = rng.integers(-2, Nkv + 40, size=B).astype(np.int32) if rng.integers(2) else None
+    nsplit = int(rng.choice([0, 1, 2, 3, 7, 16]))
+    w = wl.Workload(f"mixed{i}", B=B, H=H, H_kv=H_kv, d=d, Nkv=Nkv, top_k=top_k, dtype=dtype,
+                    gqa=gqa, seed=300 + i)
+    return w, torch.from_numpy(idx), layout, lens, nsplit
+
+
+def _run(w, q, kd, vd, bt, idx, o, lens, nsplit):
+    out = o.to(DEV)
+    sl = torch.from_numpy(lens).to(DEV) if lens is not None else None
+    if bt is not None:
+        sha.sha_decode_paged(q.to(DEV), kd, vd, bt, idx.to(DEV), w.Nkv, seqlens=sl, gqa=w.gqa,
+                             scale=w.scale, out=out, nsplit=nsplit)
+    else:
+        fn = sha.sha_decode_gqa if w.gqa else sha.sha_decode
+        fn(q.to(DEV), kd, vd, idx.to(DEV), scale=w.scale, out=out, nsplit=nsplit, seqlens=sl)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_mixed_features(i):
+    w, idx, layout, lens, nsplit = _case(i)
+    say(f"[mixed {i}] {w.dtype} gqa={w.gqa} B={w.B} H={w.H} H_kv={w.H_kv} d={w.d} "
+        f"Nkv={w.Nkv} top_k={w.top_k} layout={layout} ragged={lens is not None} nsplit={nsplit}")
+    q, k, v, _, o = wl.make_workload(w, "cpu")
+    if lens is not None:
+        k, v = ragged(w, k, v, lens)
+    bt = None
+    if layout == "bnhd":
+        kd, vd = bnhd(k), bnhd(v)
+    elif layout.startswith("paged"):
+        kd, vd, bt = paged(w, k, v, int(layout[5:]), "nphd", seed=i)
+    else:
+        kd, vd = k.to(DEV), v.to(DEV)
+    got = _run(w, q, kd, vd, bt, idx, o, lens, nsplit)
+    ref_fn = sha_decode_gqa_ref if w.gqa else sha_decode_ref
+    ref, written = ref_fn(q, k, v, idx, w.scale, seqlens=lens)
+    g64 = got.cpu().to(torch.float64).numpy()
+    assert np.isfinite(g64[written]).all(), "non-finite output in an active slot"
+    err = float(np.max(np.abs(g64[written] - ref[written]))) if written.any() else 0.0
+    assert err <= TOL[w.dtype], f"max abs error {err:.3e}"
+    wt = torch.from_numpy(written)
+    assert torch.equal(wl.raw_bits(got.cpu())[~wt], wl.raw_bits(o)[~wt]), "an inactive slot changed"
+    again = _run(w, q, kd, vd, bt, idx, o, lens, nsplit)
+    assert torch.equal(wl.raw_bits(again), wl.raw_bits(got)), "two runs differ"
+    say(f"   max abs error {err:.2e}")
