@@ -7,7 +7,11 @@ rows holding padding (-1, out of range) and repeated entries.  Each call is
 compared with the fp64 oracle on the same inputs (active slots within the
 dtype tolerance, inactive slots bit-identical to their prefill) and run twice
 for bitwise determinism.  Rows past a row's length are NaN in the cache, so
-a read beyond it shows."""
+a read beyond it shows.  Two smaller sweeps do the same for the selective MLP
+(batch rows over one to three 64-row tiles, widths and neuron counts across
+the 128-neuron and 256-column tiles, empty and padded selections) and the
+router (1-1024 heads, ragged hidden widths, top_k from 0 to H), with the
+tolerances of their own GPU test files."""
 import numpy as np
 import pytest
 import torch
@@ -94,3 +98,76 @@ def test_mixed_features(i):
     again = _run(w, q, kd, vd, bt, idx, o, lens, nsplit)
     assert torch.equal(wl.raw_bits(again), wl.raw_bits(got)), "two runs differ"
     say(f"   max abs error {err:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# selective MLP and router: seeded shapes across their tile boundaries
+# ---------------------------------------------------------------------------
+
+N_MLP = 24
+U16 = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def _mlp_case(i):
+    rng = np.random.default_rng(9500 + i)
+    dtype = ("bf16", "f16")[int(rng.integers(2))]
+    B = int(rng.integers(1, 141))                       # 1-3 tiles of 64 rows
+    d = int(rng.choice([256, 512, 768, 1280, 2048]))
+    D = max(1, int(np.exp(rng.uniform(0.0, np.log(12000.0)))))
+    k_row = int(rng.integers(0, min(D, 800) + 1))
+    pad = bool(rng.integers(2))
+    return wl.MlpWorkload(f"mixed_mlp{i}", B=B, d=d, D=D, k_row=k_row, dtype=dtype, seed=60 + i), pad
+
+
+@pytest.mark.parametrize("i", range(N_MLP))
+def test_mixed_selective_mlp(i):
+    from oracle import mlp_union_ref, selective_mlp_ref
+    w, pad = _mlp_case(i)
+    say(f"[mixed mlp {i}] {w.dtype} B={w.B} d={w.d} D={w.D} k_row={w.k_row} pad={pad}")
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    if pad and w.k_row > 0:                            # entries outside [0, D) are skipped
+        rows = rows.clone()
+        rows[0, 0] = -1
+        rows[-1, -1] = w.D
+    sel, n_sel = sha.mlp_union(rows.to(DEV), w.D)
+    y = sha.selective_mlp(x.to(DEV), w1t.to(DEV), w2t.to(DEV), sel, n_sel)
+    torch.cuda.synchronize()
+    S = mlp_union_ref(rows.numpy(), w.D)
+    assert int(n_sel.item()) == len(S)
+    assert np.array_equal(sel[:len(S)].cpu().numpy(), S)
+    ref = selective_mlp_ref(x, w1t, w2t, S)
+    got = y.cpu().double().numpy()
+    tol = 4 * U16[w.dtype] * max(1.0, float(np.abs(ref).max()))
+    err = float(np.abs(got - ref).max())
+    assert err <= tol, f"max abs error {err:.3e} > {tol:.3e}"
+    y2 = sha.selective_mlp(x.to(DEV), w1t.to(DEV), w2t.to(DEV), sel, n_sel)
+    assert torch.equal(y2, y), "two runs differ"
+    say(f"   |S|={len(S)} max abs error {err:.2e} (tol {tol:.2e})")
+
+
+N_ROUTER = 24
+
+
+def _router_case(i):
+    rng = np.random.default_rng(9700 + i)
+    dtype = ("f32", "f16", "bf16")[int(rng.integers(3))]
+    B = int(rng.integers(1, 201))
+    H = max(1, int(np.exp(rng.uniform(0.0, np.log(1024.0)))))
+    unit = 4 if dtype == "f32" else 8
+    d = unit * int(rng.integers(1, 1500 // unit * 8 + 1))
+    k = int(rng.integers(0, H + 1))
+    bias = bool(rng.integers(2))
+    B = min(B, max(1, 2_000_000 // (H * max(k, 1))))   # keeps the per-row set check short
+    return dtype, B, d, H, k, bias
+
+
+@pytest.mark.parametrize("i", range(N_ROUTER))
+def test_mixed_router(i):
+    from test_router_gpu import _check, _inputs
+    dtype, B, d, H, k, bias = _router_case(i)
+    say(f"[mixed router {i}] {dtype} B={B} d={d} H={H} k={k} bias={bias}")
+    x, w, b = _inputs(B, d, H, dtype, seed=800 + i, bias=bias)
+    idx, sc = sha.router_topk(x.to(DEV), w.to(DEV), k, bias=b.to(DEV) if b is not None else None)
+    torch.cuda.synchronize()
+    exact = _check(x, w, b, k, idx, sc)
+    say(f"   rows with an exact set check: {exact}/{B}")
