@@ -36,7 +36,8 @@ def _run(x, w1t, w2t, sel, n_sel, n_max=None):
 
 @pytest.mark.parametrize("B,k,D", [(1, 5, 100), (7, 40, 1000), (64, 300, 5000), (3, 0, 10),
                                    (5, 33, 40000), (9, 500, 100000), (64, 3686, 36864),
-                                   (2, 70000, 65537)])
+                                   (2, 70000, 65537), (16, 1638, 16384), (16, 4096, 65536),
+                                   (16, 4097, 65536), (1, 1, 1), (3, 7, 65536), (8, 3686, 36864)])
 def test_union_matches_oracle(B, k, D):
     say(f"[mlp] union B={B} k={k} D={D}")
     rng = np.random.default_rng(B * 1000 + k)
@@ -44,6 +45,23 @@ def test_union_matches_oracle(B, k, D):
     sel, n_sel = sha.mlp_union(torch.from_numpy(rows).to(DEV), D)
     torch.cuda.synchronize()
     want = mlp_union_ref(rows, D)
+    n = int(n_sel.item())
+    assert n == len(want)
+    assert np.array_equal(sel[:n].cpu().numpy(), want)
+
+
+def test_union_rows_not_16_byte_aligned():
+    """Row lists need only 4-byte alignment (here 4 bytes past a 16-byte
+    boundary)."""
+    say("[mlp] union, rows at a 4-byte offset")
+    rng = np.random.default_rng(77)
+    B, k, D = 6, 301, 5000
+    flat = torch.from_numpy(rng.integers(-2, D + 3, size=B * k + 1).astype(np.int32)).to(DEV)
+    rows = flat[1:].view(B, k)
+    assert rows.data_ptr() % 16 == 4
+    sel, n_sel = sha.mlp_union(rows, D)
+    torch.cuda.synchronize()
+    want = mlp_union_ref(rows.cpu().numpy(), D)
     n = int(n_sel.item())
     assert n == len(want)
     assert np.array_equal(sel[:n].cpu().numpy(), want)
