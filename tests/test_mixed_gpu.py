@@ -12,6 +12,8 @@ a read beyond it shows.  Two smaller sweeps do the same for the selective MLP
 the 128-neuron and 256-column tiles, empty and padded selections) and the
 router (1-1024 heads, ragged hidden widths, top_k from 0 to H), with the
 tolerances of their own GPU test files."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,7 +27,8 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from gpu_util import DEV, TOL, bnhd, paged, ragged, say
 
-N_CASES = 48
+# SHA_MIXED_CASES / _MLP / _ROUTER widen a sweep for a one-off longer check.
+N_CASES = int(os.environ.get("SHA_MIXED_CASES", 48))
 
 
 def _case(i):
@@ -104,7 +107,7 @@ def test_mixed_features(i):
 # selective MLP and router: seeded shapes across their tile boundaries
 # ---------------------------------------------------------------------------
 
-N_MLP = 24
+N_MLP = int(os.environ.get("SHA_MIXED_MLP", 24))
 U16 = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
 
@@ -145,7 +148,7 @@ def test_mixed_selective_mlp(i):
     say(f"   |S|={len(S)} max abs error {err:.2e} (tol {tol:.2e})")
 
 
-N_ROUTER = 24
+N_ROUTER = int(os.environ.get("SHA_MIXED_ROUTER", 24))
 
 
 def _router_case(i):
