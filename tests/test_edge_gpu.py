@@ -189,3 +189,37 @@ def test_raw_entry_points_auto_workspace_match_explicit():
             run_gpu(gqa, qd, kd, vd, idd, w.scale, o2, nsplit=ns)
             assert torch.equal(wl.raw_bits(o1), wl.raw_bits(o2))
             check_full(gqa, q, k, v, idx, w.scale, o, o1, TOL[dtype])
+
+
+def test_auto_workspace_on_two_streams():
+    """The internal workspace is one grow-only buffer per (device, stream):
+    calls alternating between two streams, each growing its buffer while the
+    other stream still has queued work, give the same bits as the
+    explicit-workspace form."""
+    say("[edge] internal workspace on two streams")
+    L = bd.lib()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cases, outs = [], []
+    for i, Nkv in enumerate((1024, 3000, 8192, 16384)):
+        w, q, k, v, idx, o = _case(dtype="f16", B=1, H=8, H_kv=8, top_k=2, Nkv=Nkv, seed=40 + i)
+        qd, kd, vd, idd = q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV)
+        ns = bd.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, False, q.dtype)
+        assert ns > 1  # the call needs a workspace
+        cases.append((w, qd, kd, vd, idd, o, ns))
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, (w, qd, kd, vd, idd, o, ns) in enumerate(cases):
+            s = streams[(i + rep) % 2]
+            with torch.cuda.stream(s):
+                od = o.to(DEV)
+                st = L.sha_decode_f16(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), idd.data_ptr(),
+                                      w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.scale,
+                                      od.data_ptr(), s.cuda_stream)
+            assert st == 0
+            outs.append((i, od))
+    torch.cuda.synchronize()
+    for i, od in outs:
+        w, qd, kd, vd, idd, o, ns = cases[i]
+        ref = o.to(DEV)
+        run_gpu(False, qd, kd, vd, idd, w.scale, ref, nsplit=ns)
+        assert torch.equal(wl.raw_bits(od), wl.raw_bits(ref))
