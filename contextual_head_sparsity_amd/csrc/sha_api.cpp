@@ -96,38 +96,89 @@ long long wgs_per_split(int B, int H, int H_kv, int top_k, int gqa, int dtype) {
 // stream ~22 GB/s each, so about one workgroup per CU saturates HBM and
 // splitting further only adds partials and tail.
 //
-// The matrix-core group kernel holds 2 workgroups per CU, and its best split
-// count swings with how the last round of workgroups fills the chip, so it
-// is chosen with a round model of the grid: rounds of up to 2 x CUs
-// resident workgroups, each streaming at most kGqaWgGBs while all of them
-// share kGqaHbmGBs, plus kGqaRoundUs of start-up and drain per round and
-// nothing extra for the combine.  The constants are a fit to 99 timed
-// (shape, split) pairs (8-1024 units, 1 K-32 K keys); its picks are within
-// ~2% of the best measured split on average.
+// The matrix-core group kernel runs with 4-wave workgroups (2 resident per
+// CU) or, when one split already has at least one workgroup per CU, 2-wave
+// workgroups (4 per CU, the same waves): with many units the smaller
+// workgroups fill the last round better (LLaMA-3.1-70B layer: 202 against
+// 208 us; 128 rows of 1 K keys: 58 against 65 us), with few units they
+// stream slower.  Its best split count swings with how the last round of
+// workgroups fills the chip, so it is chosen with a round model of the
+// grid: rounds of slots-per-CU x CUs resident workgroups, each streaming at
+// most a per-workgroup rate while all of them share kGqaHbmGBs, plus
+// kGqaRoundUs of start-up and drain per round and nothing extra for the
+// combine.  The 4-wave constants are a fit to 99 timed (shape, split) pairs
+// (8-1024 units, 1 K-32 K keys), whose picks are within ~2% of the best
+// measured split on average; the 2-wave rate was fitted the same way.
 constexpr int kMinSplitKeys = 512;
 constexpr int kMaxSplits = 64;
 constexpr double kGqaHbmGBs = 6800.0;
-constexpr double kGqaWgGBs = 20.0;
 constexpr double kGqaRoundUs = 4.0;
+
+struct GqaShape {
+  int waves;         // waves per workgroup
+  int slots_per_cu;  // resident workgroups per CU
+  double wg_gbs;     // streaming rate of one workgroup
+};
+constexpr GqaShape kGqaWide{4, 2, 20.0};
+constexpr GqaShape kGqaNarrow{2, 4, 13.0};
 
 void split_geometry(int Nkv, int nsplit_req, int page, int* nsplit, int* chunk);
 
 // Modelled time (us) of the group kernel with `ns` splits.
-double gqa_round_model_us(long long wgs, int Nkv, int d, int ns, int cus, int* ns_eff) {
+double gqa_round_model_us(long long wgs, int Nkv, int d, int ns, int cus, const GqaShape& sh,
+                          int* ns_eff) {
   int chunk = Nkv;
   split_geometry(Nkv, ns, 0, ns_eff, &chunk);
   const long long T = wgs * *ns_eff;
-  const long long slots = 2LL * cus;
+  const long long slots = static_cast<long long>(sh.slots_per_cu) * cus;
   const double bytes = 4.0 * chunk * d;  // K + V rows of one workgroup, 16-bit
-  const double full_rate = std::min(kGqaHbmGBs, kGqaWgGBs * static_cast<double>(slots));
+  const double full_rate = std::min(kGqaHbmGBs, sh.wg_gbs * static_cast<double>(slots));
   const long long full = T / slots, rem = T % slots;
   double t = static_cast<double>(full) *
              (bytes * static_cast<double>(slots) / full_rate / 1e3 + kGqaRoundUs);
   if (rem > 0) {
-    const double rate = std::min(kGqaWgGBs, kGqaHbmGBs / static_cast<double>(rem));
+    const double rate = std::min(sh.wg_gbs, kGqaHbmGBs / static_cast<double>(rem));
     t += bytes / rate / 1e3 + kGqaRoundUs;
   }
   return t;
+}
+
+// Best modelled split count of one workgroup shape (*t_best: its time).
+int gqa_best_split(long long wgs, int Nkv, int d, int cus, const GqaShape& sh, long long max_ns,
+                   double* t_best) {
+  int ns = 1;
+  double best = 0.0;
+  for (int c = 1; c <= max_ns; ++c) {
+    int eff = 1;
+    const double t = gqa_round_model_us(wgs, Nkv, d, c, cus, sh, &eff);
+    if (eff != c) continue;  // same geometry as a smaller request
+    if (c == 1 || t < best) {
+      best = t;
+      ns = c;
+    }
+  }
+  *t_best = best;
+  return ns;
+}
+
+long long max_splits(int Nkv) {
+  long long max_ns = Nkv / kMinSplitKeys > 1 ? Nkv / kMinSplitKeys : 1;
+  return max_ns > kMaxSplits ? kMaxSplits : max_ns;
+}
+
+// Workgroup shape of the matrix-core group kernel for one problem (it does
+// not depend on a requested split count).  2-wave workgroups only where a
+// split already has a workgroup per CU and the model puts them at least 1%
+// ahead (with few units they stream slower than the model says).
+GqaShape gqa_shape(long long wgs, int Nkv, int d, int cus) {
+  const int env = env_int("SHA_GQA_WAVES", 0);  // tuning hook: 2 or 4
+  if (env == 2) return kGqaNarrow;
+  if (env == 4) return kGqaWide;
+  if (wgs < cus) return kGqaWide;
+  double t_wide = 0.0, t_narrow = 0.0;
+  gqa_best_split(wgs, Nkv, d, cus, kGqaWide, max_splits(Nkv), &t_wide);
+  gqa_best_split(wgs, Nkv, d, cus, kGqaNarrow, max_splits(Nkv), &t_narrow);
+  return t_narrow < 0.99 * t_wide ? kGqaNarrow : kGqaWide;
 }
 
 int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int dtype,
@@ -136,20 +187,11 @@ int plan_nsplit(int B, int H, int H_kv, int Nkv, int d, int top_k, int gqa, int 
   if (wgs <= 0) return 1;
   const int cus = device_cus(num_cus);
   const bool mfma = gqa && H / H_kv > 1 && gqa_mfma(dtype);
-  long long max_ns = Nkv / kMinSplitKeys > 1 ? Nkv / kMinSplitKeys : 1;
-  if (max_ns > kMaxSplits) max_ns = kMaxSplits;
+  const long long max_ns = max_splits(Nkv);
   long long ns = 1;
   if (mfma) {
-    double best = 0.0;
-    for (int c = 1; c <= max_ns; ++c) {
-      int eff = 1;
-      const double t = gqa_round_model_us(wgs, Nkv, d, c, cus, &eff);
-      if (eff != c) continue;  // same geometry as a smaller request
-      if (c == 1 || t < best) {
-        best = t;
-        ns = c;
-      }
-    }
+    double t = 0.0;
+    ns = gqa_best_split(wgs, Nkv, d, cus, gqa_shape(wgs, Nkv, d, cus), max_ns, &t);
   } else {
     ns = (cus + wgs - 1) / wgs;
     if (ns > max_ns) ns = max_ns;
@@ -315,6 +357,8 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   a.G = p.H / p.H_kv;
   a.nsplit = ns;
   a.chunk = chunk;
+  a.waves = gqa_shape(wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa, p.dtype), p.Nkv, p.d,
+                      device_cus(0)).waves;
   a.scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
   a.layout = kind;
   if (p.kv) {

@@ -34,6 +34,7 @@ struct Args {
   int G;                // H / H_kv
   int nsplit;           // effective split count (every split holds >= 1 key)
   int chunk;            // keys per split (last split may hold fewer)
+  int waves;            // waves per workgroup of the matrix-core group kernel (2 or 4)
   float scale_log2;     // scale * log2(e): scores are kept in the base-2 domain
   // KV addressing (strided / paged layouts); strides in elements.
   int layout;           // KvLayout

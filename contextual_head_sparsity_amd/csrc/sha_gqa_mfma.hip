@@ -321,9 +321,8 @@ __global__ __launch_bounds__(WAVES * 64) void sha_decode_gqa_mfma_kernel(Args a)
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int WAVES>
 hipError_t launch_t(const Args& a, hipStream_t st) {
-  constexpr int WAVES = 4;
   const unsigned nchunk = (a.G + kCols - 1) / kCols;
   const dim3 grid(static_cast<unsigned>(a.B) * a.top_k * nchunk * a.nsplit), block(WAVES * 64);
   if (a.layout == kKvStrided)
@@ -337,11 +336,16 @@ hipError_t launch_t(const Args& a, hipStream_t st) {
   return e;
 }
 
+template <int DT, int D>
+hipError_t launch_w(const Args& a, hipStream_t st) {
+  return a.waves == 2 ? launch_t<DT, D, 2>(a, st) : launch_t<DT, D, 4>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_gqa_mfma(const Args& a, int dtype, int d, hipStream_t st) {
-  if (dtype == kF16) return d == 64 ? launch_t<kF16, 64>(a, st) : launch_t<kF16, 128>(a, st);
-  return d == 64 ? launch_t<kBF16, 64>(a, st) : launch_t<kBF16, 128>(a, st);
+  if (dtype == kF16) return d == 64 ? launch_w<kF16, 64>(a, st) : launch_w<kF16, 128>(a, st);
+  return d == 64 ? launch_w<kBF16, 64>(a, st) : launch_w<kBF16, 128>(a, st);
 }
 
 }  // namespace sha

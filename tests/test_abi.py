@@ -103,12 +103,15 @@ def test_planner_and_workspace_accounting():
     assert L.sha_plan_nsplit(16, 32, 32, 1024, 128, 16, 0, 1, 256) == 1
     assert L.sha_plan_nsplit(4, 32, 32, 4096, 128, 16, 0, 1, 256) == 4
     assert L.sha_plan_nsplit(1, 32, 32, 4096, 128, 16, 0, 1, 256) == 8
-    # Group (matrix-core) kernel: round model over 2 resident workgroups per
-    # CU.  The LLaMA-3.1-70B layer (320 units) splits 3 ways (960 workgroups,
-    # a nearly full second round); 512 units fill one round unsplit; 8 units
-    # split down to the 512-key minimum.
-    assert L.sha_plan_nsplit(64, 64, 8, 8192, 128, 5, 1, 2, 256) == 3
+    # Group (matrix-core) kernel: round model of the grid.  The LLaMA-3.1-70B
+    # layer (320 units, more than one workgroup per CU) takes 2-wave
+    # workgroups, 4 per CU, and splits 2 ways (640 workgroups, one round);
+    # 512 units keep 4-wave workgroups and fill one round unsplit; 128 rows of
+    # 1 K keys (640 units) take 2-wave workgroups unsplit; 8 units split down
+    # to the 512-key minimum.
+    assert L.sha_plan_nsplit(64, 64, 8, 8192, 128, 5, 1, 2, 256) == 2
     assert L.sha_plan_nsplit(64, 64, 8, 8192, 128, 8, 1, 2, 256) == 1
+    assert L.sha_plan_nsplit(128, 64, 8, 1024, 128, 5, 1, 2, 256) == 1
     assert L.sha_plan_nsplit(2, 64, 8, 8192, 128, 4, 1, 2, 256) == 16
     # The f32 group kernel (vector ALUs) keeps the one-workgroup-per-CU rule.
     assert L.sha_plan_nsplit(64, 64, 8, 8192, 128, 5, 1, 0, 256) == 1

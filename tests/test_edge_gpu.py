@@ -223,3 +223,46 @@ def test_auto_workspace_on_two_streams():
         ref = o.to(DEV)
         run_gpu(False, qd, kd, vd, idd, w.scale, ref, nsplit=ns)
         assert torch.equal(wl.raw_bits(od), wl.raw_bits(ref))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("G,d", [(8, 128), (17, 64)])
+@pytest.mark.parametrize("layout", ["contig", "bnhd", "paged16"])
+def test_gqa_two_and_four_wave_workgroups(dtype, G, d, layout, monkeypatch):
+    """The group kernel's two workgroup shapes (2 or 4 waves; the planner
+    picks one per problem, SHA_GQA_WAVES forces it) against the oracle at the
+    planned and at forced split counts, with ragged lengths and three cache
+    layouts."""
+    from gpu_util import bnhd, paged, ragged
+    from oracle import sha_decode_gqa_ref
+    H_kv = 4
+    w = wl.Workload("wide", B=40, H=H_kv * G, H_kv=H_kv, d=d, Nkv=1100, top_k=3, dtype=dtype,
+                    gqa=True, seed=G + d)
+    q, k, v, idx, o = wl.make_workload(w, "cpu")
+    lens = np.random.default_rng(5).integers(0, w.Nkv + 30, size=w.B).astype(np.int32)
+    k, v = ragged(w, k, v, lens)
+    sl = torch.from_numpy(lens).to(DEV)
+    ref, written = sha_decode_gqa_ref(q, k, v, idx, w.scale, seqlens=lens)
+    wt = torch.from_numpy(written)
+    if layout == "paged16":
+        kd, vd, bt = paged(w, k, v, 16, "nphd", seed=3)
+    else:
+        kd, vd = (bnhd(k), bnhd(v)) if layout == "bnhd" else (k.to(DEV), v.to(DEV))
+    for waves in ("2", "4"):
+        monkeypatch.setenv("SHA_GQA_WAVES", waves)
+        for nsplit in (0, 1, 2):
+            say(f"[edge] group workgroups of {waves} waves {dtype} G={G} d={d} {layout} "
+                f"nsplit={nsplit}")
+            od = o.to(DEV)
+            if layout == "paged16":
+                sha.sha_decode_paged(q.to(DEV), kd, vd, bt, idx.to(DEV), w.Nkv, seqlens=sl,
+                                     gqa=True, scale=w.scale, out=od, nsplit=nsplit)
+            else:
+                sha.sha_decode_gqa(q.to(DEV), kd, vd, idx.to(DEV), scale=w.scale, out=od,
+                                   nsplit=nsplit, seqlens=sl)
+            torch.cuda.synchronize()
+            g64 = od.cpu().to(torch.float64).numpy()
+            assert np.isfinite(g64[written]).all()
+            err = float(np.max(np.abs(g64[written] - ref[written])))
+            assert err <= TOL[dtype], f"max abs error {err:.3e}"
+            assert torch.equal(wl.raw_bits(od.cpu())[~wt], wl.raw_bits(o)[~wt])
