@@ -357,8 +357,10 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
   a.G = p.H / p.H_kv;
   a.nsplit = ns;
   a.chunk = chunk;
-  a.waves = gqa_shape(wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa, p.dtype), p.Nkv, p.d,
-                      device_cus(0)).waves;
+  a.waves = gqa_eff && gqa_mfma(p.dtype)
+                ? gqa_shape(wgs_per_split(p.B, p.H, p.H_kv, p.top_k, p.gqa, p.dtype), p.Nkv, p.d,
+                            device_cus(0)).waves
+                : 4;
   a.scale_log2 = static_cast<float>(static_cast<double>(p.scale) * 1.4426950408889634);
   a.layout = kind;
   if (p.kv) {
