@@ -266,3 +266,17 @@ def test_gqa_two_and_four_wave_workgroups(dtype, G, d, layout, monkeypatch):
             err = float(np.max(np.abs(g64[written] - ref[written])))
             assert err <= TOL[dtype], f"max abs error {err:.3e}"
             assert torch.equal(wl.raw_bits(od.cpu())[~wt], wl.raw_bits(o)[~wt])
+
+
+@pytest.mark.parametrize("gqa", [False, True])
+def test_large_batch_short_rows(gqa):
+    """Thousands of batch rows with short caches: grids far past one round,
+    against the oracle on every slot."""
+    say(f"[edge] large batch gqa={gqa}")
+    if gqa:
+        w, q, k, v, idx, o = _case(dtype="bf16", B=3000, H=16, H_kv=4, d=64, Nkv=40, top_k=2,
+                                   gqa=True, seed=91)
+    else:
+        w, q, k, v, idx, o = _case(dtype="f16", B=4096, H=8, H_kv=8, d=64, Nkv=40, top_k=3,
+                                   seed=92)
+    _run_check(w, q, k, v, idx, o)
