@@ -106,8 +106,28 @@ def pin_union(impl):
     assert list(impl.union(np.full((2, 3), -1), 8)) == []
 
 
+def pin_padding_entries_select_nothing(impl):
+    """Entries outside [0, D) (-1, D, D + 7) select no neuron: the result
+    equals the call on the filtered list, and a selection of padding alone
+    gives zeros.  The last neuron fires for every row here, so reading -1 as
+    neuron D - 1 would change the result."""
+    rng = np.random.default_rng(46)
+    D = 12
+    x, w1t, w2t = _rand(rng, 3, 5, D)
+    x = np.abs(x)
+    w1t[D - 1] = np.abs(w1t[D - 1]) + 0.5
+    valid = np.array([4, 0, 9, 2])
+    padded = np.array([-1, 4, D, 0, 9, -1, D + 7, 2])
+    np.testing.assert_allclose(impl.mlp(x, w1t, w2t, padded), impl.mlp(x, w1t, w2t, valid),
+                               rtol=0, atol=1e-14)
+    assert np.array_equal(impl.mlp(x, w1t, w2t, np.array([-1, D, D + 7])), np.zeros((3, 5)))
+    ref = _brute(x.tolist(), w1t.tolist(), w2t.tolist(), valid.tolist())
+    np.testing.assert_allclose(impl.mlp(x, w1t, w2t, padded), ref, rtol=0, atol=1e-12)
+
+
 PINS = [pin_dense_equals_torch_mlp, pin_golden, pin_brute_force,
-        pin_cover_of_active_neurons_is_exact, pin_invariants, pin_union]
+        pin_cover_of_active_neurons_is_exact, pin_invariants, pin_union,
+        pin_padding_entries_select_nothing]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -121,6 +141,12 @@ def _mutant_mlp(kind):
         S = np.asarray(sel, dtype=np.int64).reshape(-1)
         if kind == "ignores_selection":
             S = np.arange(W1t.shape[0])
+        if kind == "padding_wraps":
+            S = S[S < W1t.shape[0]]          # -1 kept: numpy reads it as neuron D - 1
+        elif kind == "padding_clamped":
+            S = np.clip(S, 0, W1t.shape[0] - 1)
+        elif kind != "ignores_selection":
+            S = S[(S >= 0) & (S < W1t.shape[0])]
         if S.size == 0:
             return np.zeros((X.shape[0], X.shape[1]))
         pre = X @ W1t[S].T
@@ -155,7 +181,8 @@ def _mutant_union(kind):
 
 
 MLP_MUTANTS = ["ignores_selection", "no_relu", "abs_instead_of_relu", "w1_for_output",
-               "relu_after_output", "selects_output_by_position"]
+               "relu_after_output", "selects_output_by_position", "padding_wraps",
+               "padding_clamped"]
 UNION_MUTANTS = ["keeps_padding", "first_row_only", "not_deduplicated"]
 
 

@@ -438,3 +438,90 @@ def test_planted_mistake_is_caught(kind, monkeypatch):
         impl = types.SimpleNamespace(mha=so.sha_decode_ref, gqa=_mutant_gqa(kind))
     failed = _pins_failed(impl)
     assert failed, f"mutant {kind} passed every pin"
+
+
+# ----------------------------------------------------------------------------
+# Sampled-unit form (sha_units_ref): the checker of the full-size GPU tests.
+# Pinned against the whole-call oracle at the same slots (bitwise: the same
+# definition evaluated on the same widened operands), closed forms and brute
+# force; planted mistakes must each fail.
+# ----------------------------------------------------------------------------
+
+def _gather_units(q, k, v, slots, G):
+    qs = np.stack([q[b, h, 0] for b, h in slots])
+    ks = np.stack([k[b, h // G] for b, h in slots])
+    vs = np.stack([v[b, h // G] for b, h in slots])
+    return qs, ks, vs
+
+
+def upin_equals_whole_call(units):
+    """Gathered (q, K, V) of active slots give bitwise the whole-call result,
+    for f32-exact and f16-rounded operands and a scale that float32 rounds."""
+    rng = np.random.default_rng(61)
+    for (B, H, H_kv, Nkv, d, top_k) in [(3, 6, 3, 13, 8, 2), (2, 4, 4, 40, 16, 4)]:
+        q, k, v = _rand(rng, B, H, H_kv, Nkv, d, scale_q=2.0)
+        q, k, v = (torch.from_numpy(a).to(torch.float16) for a in (q, k, v))
+        idx = _sorted_rows(rng, B, H, top_k)
+        scale = 0.1  # not a float32 value: both forms must round it alike
+        O, w = so.sha_decode_ref(q, k, v, idx, scale)
+        slots = [tuple(x) for x in np.argwhere(w)]
+        got = units(*_gather_units(q.numpy(), k.numpy(), v.numpy(), slots, H // H_kv), scale)
+        assert got.shape == (len(slots), d)
+        for i, (b, h) in enumerate(slots):
+            assert np.array_equal(got[i], O[b, h, 0]), (b, h)
+
+
+def upin_closed_forms(units):
+    """One key gives that key's value row; equal scores give the mean row."""
+    rng = np.random.default_rng(62)
+    qs, ks, vs = rng.standard_normal((3, 5)), rng.standard_normal((3, 1, 5)), rng.standard_normal((3, 1, 5))
+    assert np.array_equal(units(qs, ks, vs, 0.5), vs[:, 0])
+    ks = rng.standard_normal((3, 7, 5))
+    vs = rng.standard_normal((3, 7, 5))
+    qz = np.zeros((3, 5))
+    np.testing.assert_allclose(units(qz, ks, vs, 0.5), vs.mean(axis=1), rtol=0, atol=1e-14)
+
+
+def upin_brute_force(units):
+    rng = np.random.default_rng(63)
+    qs, ks, vs = rng.standard_normal((4, 6)) * 2, rng.standard_normal((4, 9, 6)), rng.standard_normal((4, 9, 6))
+    s = float(np.float32(0.3))
+    got = units(qs, ks, vs, s)
+    for i in range(4):
+        ref = _brute_force_one(qs[i].tolist(), ks[i].tolist(), vs[i].tolist(), s)
+        np.testing.assert_allclose(got[i], ref, rtol=0, atol=1e-12)
+
+
+UNIT_PINS = [upin_equals_whole_call, upin_closed_forms, upin_brute_force]
+
+
+@pytest.mark.parametrize("pin", UNIT_PINS, ids=lambda p: p.__name__)
+def test_units_oracle_pin(pin):
+    pin(so.sha_units_ref)
+
+
+def _mutant_units(kind):
+    def units(q_rows, k_slabs, v_slabs, scale):
+        qs, Ks, Vs = so.to_f64(q_rows), so.to_f64(k_slabs), so.to_f64(v_slabs)
+        s = float(scale) if kind == "unrounded_scale" else float(np.float32(scale))
+        n = qs.shape[0]
+        out = []
+        for i in range(n):
+            j = 0 if kind == "first_unit_only" else i
+            K, V = (Vs[j], Ks[j]) if kind == "k_v_swapped" else (Ks[j], Vs[j])
+            out.append(so.attend_one(qs[i], K, V, s))
+        res = np.stack(out)
+        return res[::-1].copy() if kind == "reversed_order" else res
+    return units
+
+
+@pytest.mark.parametrize("kind", ["unrounded_scale", "first_unit_only", "k_v_swapped",
+                                  "reversed_order"])
+def test_planted_units_mistake_is_caught(kind):
+    failed = []
+    for pin in UNIT_PINS:
+        try:
+            pin(_mutant_units(kind))
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {kind} passed every pin"
