@@ -142,6 +142,10 @@ def workspace_bytes_paged(B, H, H_kv, Nkv, d, top_k, gqa=False, dtype=torch.floa
                                         num_cus, ctypes.byref(lay))
 
 
+def _stream_for(dev, stream):
+    return torch.cuda.current_stream(dev) if stream is None else stream
+
+
 def _prepare(q, k, v, index, scale, out, gqa, paged=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -207,36 +211,50 @@ def _layout(k, v, seqlens, block_table, B, Nkv):
 def _call(gqa, q, k, v, index, scale, out, nsplit, workspace, stream, seqlens=None,
           block_table=None, Nkv=None):
     paged = block_table is not None
-    B, H, H_kv, Nk, d, top_k, index, scale, out = _prepare(q, k, v, index, scale, out, gqa, paged)
-    if paged:
-        if Nkv is None:
-            raise ValueError("a paged call needs Nkv (the longest row)")
-    else:
-        Nkv = Nk
-    lay, keep = _layout(k, v, seqlens, block_table, B, Nkv)
-    L = lib()
-    dt = _DT[q.dtype]
-    lp = ctypes.byref(lay) if lay is not None else None
-    need = L.sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0, lp)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    with torch.cuda.device(q.device):
-        if lay is None:
-            name = "sha_decode_gqa_ex" if gqa else "sha_decode_ex"
-            st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H,
-                                  H_kv, Nkv, d, top_k, scale, out.data_ptr(), stream.cuda_stream,
-                                  dt, nsplit, ws_ptr, need)
+    if isinstance(q, torch.Tensor) and q.is_cuda:
+        stream = _stream_for(q.device, stream)
+    # Every temporary (index copy, zero-filled out, workspace) is made on the
+    # call's stream, so the kernel sees it ready and the allocator does not
+    # hand its memory to other streams while the kernel may still read it.
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        B, H, H_kv, Nk, d, top_k, index, scale, out = _prepare(q, k, v, index, scale, out, gqa,
+                                                               paged)
+        if paged:
+            if Nkv is None:
+                raise ValueError("a paged call needs Nkv (the longest row)")
         else:
-            name = "sha_decode_gqa_kv" if gqa else "sha_decode_kv"
-            st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(), B, H,
-                                  H_kv, Nkv, d, top_k, scale, out.data_ptr(), stream.cuda_stream,
-                                  dt, lp, nsplit, ws_ptr, need)
-    del keep
+            Nkv = Nk
+        lay, keep = _layout(k, v, seqlens, block_table, B, Nkv)
+        L = lib()
+        dt = _DT[q.dtype]
+        lp = ctypes.byref(lay) if lay is not None else None
+        need = L.sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0, lp)
+        if need and (workspace is None or not workspace.is_cuda or
+                     workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if need else None
+        with torch.cuda.device(q.device):
+            if lay is None:
+                name = "sha_decode_gqa_ex" if gqa else "sha_decode_ex"
+                st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(),
+                                      B, H, H_kv, Nkv, d, top_k, scale, out.data_ptr(),
+                                      stream.cuda_stream, dt, nsplit, ws_ptr, need)
+            else:
+                name = "sha_decode_gqa_kv" if gqa else "sha_decode_kv"
+                st = getattr(L, name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), index.data_ptr(),
+                                      B, H, H_kv, Nkv, d, top_k, scale, out.data_ptr(),
+                                      stream.cuda_stream, dt, lp, nsplit, ws_ptr, need)
+        del keep
     _check(st, name)
     return out
+
+
+class _nullctx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
 
 
 def sha_decode(q, k, v, batch_head_index, scale=None, out=None, nsplit=0, workspace=None,
@@ -248,6 +266,11 @@ def sha_decode(q, k, v, batch_head_index, scale=None, out=None, nsplit=0, worksp
     permute(0, 2, 1, 3)); batch_head_index [B, top_k]; seqlens [B] (optional)
     limits row b to its first seqlens[b] keys.  Slots of `out` not named by
     the index are left untouched.
+
+    stream (default: the current stream) runs the call; the inputs must be
+    ready on it, as for any operation on that stream.  workspace: a device
+    tensor for the split partials (allocated on the stream when None or too
+    small).
     """
     return _call(False, q, k, v, batch_head_index, scale, out, nsplit, workspace, stream, seqlens)
 
@@ -286,26 +309,29 @@ def _dev_i32(t, name):
 
 def mlp_union(row_neurons, D, sel=None, n_sel=None, stream=None, workspace=None):
     """Sorted union of the rows' neuron lists (entries outside [0, D) skipped),
-    on the device: returns (sel [min(D, B*k)] int32, n_sel [1] int32)."""
-    rows = _dev_i32(row_neurons, "row_neurons")
-    if rows.dim() != 2:
-        raise ValueError("row_neurons must be [B, k]")
-    B, k = rows.shape
-    cap = max(1, min(D, B * k))
-    if sel is None:
-        sel = torch.empty(cap, dtype=torch.int32, device=rows.device)
-    elif sel.numel() < cap or sel.dtype != torch.int32 or not sel.is_contiguous():
-        raise ValueError(f"sel must be a contiguous int32 tensor of >= {cap} entries")
-    if n_sel is None:
-        n_sel = torch.empty(1, dtype=torch.int32, device=rows.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(rows.device)
-    need = lib().sha_mlp_union_workspace_bytes(D)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
-    with torch.cuda.device(rows.device):
-        st = lib().sha_mlp_union(rows.data_ptr(), B, k, D, sel.data_ptr(), n_sel.data_ptr(),
-                                 stream.cuda_stream, workspace.data_ptr(), need)
+    on the device: returns (sel [min(D, B*k)] int32, n_sel [1] int32).
+    Runs on `stream` (default: the current stream); temporaries are made there."""
+    if not isinstance(row_neurons, torch.Tensor) or not row_neurons.is_cuda:
+        raise ValueError("row_neurons must be a device tensor")
+    stream = _stream_for(row_neurons.device, stream)
+    with torch.cuda.stream(stream):
+        rows = _dev_i32(row_neurons, "row_neurons")
+        if rows.dim() != 2:
+            raise ValueError("row_neurons must be [B, k]")
+        B, k = rows.shape
+        cap = max(1, min(D, B * k))
+        if sel is None:
+            sel = torch.empty(cap, dtype=torch.int32, device=rows.device)
+        elif sel.numel() < cap or sel.dtype != torch.int32 or not sel.is_contiguous():
+            raise ValueError(f"sel must be a contiguous int32 tensor of >= {cap} entries")
+        if n_sel is None:
+            n_sel = torch.empty(1, dtype=torch.int32, device=rows.device)
+        need = lib().sha_mlp_union_workspace_bytes(D)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
+        with torch.cuda.device(rows.device):
+            st = lib().sha_mlp_union(rows.data_ptr(), B, k, D, sel.data_ptr(), n_sel.data_ptr(),
+                                     stream.cuda_stream, workspace.data_ptr(), need)
     _check(st, "sha_mlp_union")
     return sel, n_sel
 
@@ -318,7 +344,8 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
     """y = relu(x w1t[S]^T) w2t[S], S = sel[:n_sel] (device count).
 
     x [B, d]; w1t, w2t [D, d] (neuron-major: W1^T and W2^T); f16 or bf16.
-    n_max bounds the count (default: sel.numel()).
+    n_max bounds the count (default: sel.numel()); sel must hold at least
+    n_max entries.  Runs on `stream` (default: the current stream).
     """
     for name, t in (("x", x), ("w1t", w1t), ("w2t", w2t)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
@@ -329,24 +356,26 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
     D = w1t.shape[0]
     if w1t.shape != (D, d) or w2t.shape != (D, d):
         raise ValueError("w1t and w2t must be [D, d]")
-    sel = _dev_i32(sel, "sel")
-    n_sel = _dev_i32(n_sel, "n_sel")
-    if n_max is None:
-        n_max = min(sel.numel(), D)
-    if out is None:
-        out = torch.empty_like(x)
-    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like x")
-    L = lib()
-    need = L.sha_selective_mlp_workspace_bytes(B, d, D, n_max, 0)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    with torch.cuda.device(x.device):
-        st = L.sha_selective_mlp(x.data_ptr(), w1t.data_ptr(), w2t.data_ptr(), sel.data_ptr(),
-                                 n_sel.data_ptr(), n_max, B, d, D, out.data_ptr(),
-                                 stream.cuda_stream, _DT[x.dtype], workspace.data_ptr(), need)
+    stream = _stream_for(x.device, stream)
+    with torch.cuda.stream(stream):
+        sel = _dev_i32(sel, "sel")
+        n_sel = _dev_i32(n_sel, "n_sel")
+        if n_max is None:
+            n_max = min(sel.numel(), D)
+        if n_max > sel.numel():
+            raise ValueError(f"n_max = {n_max} exceeds the {sel.numel()} entries of sel")
+        if out is None:
+            out = torch.empty_like(x)
+        elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor like x")
+        L = lib()
+        need = L.sha_selective_mlp_workspace_bytes(B, d, D, n_max, 0)
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        with torch.cuda.device(x.device):
+            st = L.sha_selective_mlp(x.data_ptr(), w1t.data_ptr(), w2t.data_ptr(), sel.data_ptr(),
+                                     n_sel.data_ptr(), n_max, B, d, D, out.data_ptr(),
+                                     stream.cuda_stream, _DT[x.dtype], workspace.data_ptr(), need)
     _check(st, "sha_selective_mlp")
     return out
 
@@ -358,7 +387,8 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
 def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
     """Attention router on the device: scores = x w^T (+ bias), the top_k heads
     per row in ascending order.  x [B, d], w [H, d] (f32 / f16 / bf16), bias
-    [H] fp32.  Returns (index [B, top_k] int32, scores [B, H] fp32)."""
+    [H] fp32.  Returns (index [B, top_k] int32, scores [B, H] fp32).  Runs on
+    `stream` (default: the current stream)."""
     for name, t in (("x", x), ("w", w)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
             raise ValueError(f"{name} must be a contiguous 2-D device tensor")
@@ -368,21 +398,27 @@ def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
     H = w.shape[0]
     if w.shape[1] != d:
         raise ValueError("w must be [H, d]")
-    if bias is not None:
-        if not bias.is_cuda or bias.dtype != torch.float32 or bias.numel() != H:
-            raise ValueError("bias must be a float32 device tensor of H entries")
-        bias = bias.contiguous()
-    if index is None:
-        index = torch.empty((B, top_k), dtype=torch.int32, device=x.device)
-    if scores is None:
-        scores = torch.empty((B, H), dtype=torch.float32, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
-    with torch.cuda.device(x.device):
-        st = lib().sha_router_topk(x.data_ptr(), w.data_ptr(),
-                                   bias.data_ptr() if bias is not None else None, B, d, H, top_k,
-                                   index.data_ptr(), scores.data_ptr(), stream.cuda_stream,
-                                   _DT[x.dtype])
+    stream = _stream_for(x.device, stream)
+    with torch.cuda.stream(stream):
+        if bias is not None:
+            if not bias.is_cuda or bias.dtype != torch.float32 or bias.numel() != H:
+                raise ValueError("bias must be a float32 device tensor of H entries")
+            bias = bias.contiguous()
+        if index is None:
+            index = torch.empty((B, top_k), dtype=torch.int32, device=x.device)
+        elif index.dtype != torch.int32 or not index.is_contiguous() or \
+                tuple(index.shape) != (B, top_k):
+            raise ValueError("index must be a contiguous int32 [B, top_k] tensor")
+        if scores is None:
+            scores = torch.empty((B, H), dtype=torch.float32, device=x.device)
+        elif scores.dtype != torch.float32 or not scores.is_contiguous() or \
+                tuple(scores.shape) != (B, H):
+            raise ValueError("scores must be a contiguous float32 [B, H] tensor")
+        with torch.cuda.device(x.device):
+            st = lib().sha_router_topk(x.data_ptr(), w.data_ptr(),
+                                       bias.data_ptr() if bias is not None else None, B, d, H,
+                                       top_k, index.data_ptr(), scores.data_ptr(),
+                                       stream.cuda_stream, _DT[x.dtype])
     _check(st, "sha_router_topk")
     return index, scores
 
@@ -393,6 +429,24 @@ def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _step_check(i, L, B, top_k, n_sel):
+    def need(name, dtype, shape=None):
+        t = L.get(name)
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype \
+                or not t.is_contiguous() or (shape is not None and tuple(t.shape) != shape):
+            want = f"contiguous {dtype} device tensor" + (f" of shape {shape}" if shape else "")
+            raise ValueError(f"layer {i}: {name} must be a {want}")
+    need("seqlens", torch.int32, (B,))
+    need("block_table", torch.int32)
+    if L.get("block_table") is not None and L["block_table"].dim() != 2:
+        raise ValueError(f"layer {i}: block_table must be [B, max_pages]")
+    if not L.get("dense", False):
+        need("index", torch.int32, (B, top_k))
+        need("router_scores", torch.float32, (B, n_sel))
 
 
 class DecodeStep:
@@ -407,7 +461,11 @@ class DecodeStep:
     [B, max_pages] int32 table, as for sha_decode_paged; Nkv is then the
     longest row).
     The tensors are referenced for the life of the step: refresh their
-    contents in place between runs.
+    contents in place between runs.  A tensor the step would otherwise have
+    to copy (seqlens or block_table not contiguous int32, index not
+    contiguous int32 [B, top_k], router_scores not contiguous float32
+    [B, H] -- [B, H_kv] for group layers) is rejected with ValueError, since
+    in-place refreshes of the original would never reach the copy.
     """
 
     def __init__(self, B, H, H_kv, Nkv, d, top_k, dtype, layers, gqa=False, scale=None,
@@ -418,7 +476,9 @@ class DecodeStep:
                          float(scale if scale is not None else 1.0 / math.sqrt(d)), _DT[dtype],
                          router_d, mlp_d, mlp_D, mlp_k)
         arr = (StepLayer * len(layers))()
+        n_sel = H_kv if gqa else H
         for i, L in enumerate(layers):
+            _step_check(i, L, B, top_k, n_sel)
             for name in ("router_x", "router_w", "router_bias", "router_scores", "index", "q",
                          "k", "v", "o", "mlp_x", "mlp_w1t", "mlp_w2t", "mlp_y", "mlp_rows"):
                 t = L.get(name)

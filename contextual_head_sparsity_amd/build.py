@@ -7,6 +7,7 @@ library atomically.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -45,16 +46,21 @@ def build(verbose: bool = True) -> str:
     hipcc = _hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    objs, cmds = [], []
     for src in ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_mlp.hip", "sha_router.hip"):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        _run([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
-              os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in ("sha_api.cpp", "sha_step.cpp"):
         obj = os.path.join(objdir, src.replace(".cpp", ".o"))
-        _run([hipcc, "-c", *COMMON, os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, "-c", *COMMON, os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # The translation units are independent: compile them side by side.
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+        for f in [pool.submit(_run, c) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)

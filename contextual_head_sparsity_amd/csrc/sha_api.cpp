@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "sha_launch.h"
 
@@ -275,9 +276,23 @@ size_t partial_bytes(int B, int H, int H_kv, int d, int top_k, int gqa, int nspl
 sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // Internal workspace for the calls without an explicit workspace: one
-// grow-only buffer per (device, stream), kept until the process ends.
+// grow-only buffer per (device, stream).  A buffer that is
+// outgrown is kept, not freed, until the process ends: work already queued
+// on the stream, or a graph that captured a call, may still use it.  Growing
+// needs an allocation, which a stream under capture cannot take: such a call
+// returns SHA_ERR_WORKSPACE instead.
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> g_ws;
+std::vector<void*> g_ws_retired;
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;  // unknown: do not allocate
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
 
 sha_status run_auto(const Problem& p, hipStream_t stream) {
   bool empty = false;
@@ -298,22 +313,14 @@ sha_status run_auto(const Problem& p, hipStream_t stream) {
   }
   auto& slot = g_ws[{dev, stream}];
   if (slot.second < need) {
-    if (slot.first) {
-      // The old buffer may still be read by queued work on this stream.
-      e = hipStreamSynchronize(stream);
-      if (e == hipSuccess) e = hipFree(slot.first);
-      slot = {nullptr, 0};
-      if (e != hipSuccess) {
-        g_last_hip_error = e;
-        return SHA_ERR_HIP;
-      }
-    }
+    if (stream_capturing(stream)) return SHA_ERR_WORKSPACE;
     void* ptr = nullptr;
     e = hipMalloc(&ptr, need);
     if (e != hipSuccess) {
       g_last_hip_error = e;
       return SHA_ERR_HIP;
     }
+    if (slot.first) g_ws_retired.push_back(slot.first);
     slot = {ptr, need};
   }
   return run(p, ns, slot.first, slot.second, stream);

@@ -71,7 +71,7 @@ typedef enum {
   SHA_ERR_INVALID_ARG = 1,  /* bad scalar (negative size, H % H_kv != 0, top_k out of range, Nkv < 1, non-finite scale) or null pointer */
   SHA_ERR_UNSUPPORTED = 2,  /* head dimension other than 64 / 128, unknown dtype, group size > 64 */
   SHA_ERR_MISALIGNED = 3,   /* pointer alignment below what the 128-bit loads need */
-  SHA_ERR_WORKSPACE = 4,    /* workspace null or smaller than sha_workspace_bytes() */
+  SHA_ERR_WORKSPACE = 4,    /* workspace null or smaller than sha_workspace_bytes(), or an internal workspace that would have to grow on a stream under capture */
   SHA_ERR_HIP = 5           /* a HIP runtime call or launch failed */
 } sha_status;
 
@@ -81,10 +81,16 @@ typedef enum {
  * H_kv < H (H % H_kv == 0, G = H / H_kv) head h reads KV head h / G.
  *   scale : score scale, normally 1/sqrt(d) (Algorithm 1's s); must be finite.
  *   stream: HIP stream to enqueue on (0 = the null stream).
- * The library picks the split count and uses an internal, per-device cached
- * workspace when it needs one (allocated on first need, grown, kept until
- * the process ends; calls from several host threads are serialised around
- * it).  Callers that must not allocate use sha_decode_ex.
+ * The library picks the split count and uses an internal workspace when it
+ * needs one: one buffer per (device, stream), allocated on first
+ * need and replaced by a larger one when a call needs more; outgrown buffers
+ * are kept, not freed, until the process ends (queued work or a captured
+ * graph may still use them).  Calls from several host threads are
+ * serialised around it.  On a stream that is being captured into a graph the
+ * library does not allocate: a call that would need to grow the workspace
+ * then returns SHA_ERR_WORKSPACE and enqueues nothing (a call the existing
+ * workspace covers is captured normally).  Callers that must not allocate
+ * use sha_decode_ex.
  * The three typed forms take exactly these arguments; sha_decode adds dtype.
  */
 sha_status sha_decode_f32(const void* q, const void* k, const void* v,

@@ -2,11 +2,13 @@
 
 A step strings router -> selective head attention -> selective MLP over
 several layers, layer 0 dense, and may run as one captured HIP graph.  Every
-run is compared bit for bit with the same calls made one by one (each of
-those is pinned to the fp64 oracle by its own tests), and layer 0 is also
-checked against the oracle directly.  Graph replays are interleaved with
-in-place input updates, other device work and synchronisations, and every
-replay is checked.
+run is compared bit for bit with the same calls made one by one, and every
+layer's attention output is checked against the fp64 oracle on the index
+the step's own router wrote (all heads for the dense layer), with that
+layer's per-row lengths and page layout.  Graph replays are interleaved with
+in-place input updates (queries, router inputs, MLP rows and the per-row
+lengths), other device work and synchronisations, and every replay is
+checked.
 """
 import numpy as np
 import pytest
@@ -54,7 +56,9 @@ def _layers(cfg, n_layers, mlp, seed, seqlens_layer=None, paged=None):
         w = wl.Workload("step", B=B, H=H, H_kv=H_kv, d=d, Nkv=Nkv, top_k=cfg["top_k"],
                         dtype=cfg["dname"], gqa=cfg["gqa"], seed=seed + l)
         q, k, v = wl.make_qkv(w, DEV)
-        L = dict(q=q, k=k, v=v, o=wl.sentinel_like(w, DEV), dense=(l == 0))
+        # k_ref / v_ref: the contiguous cache the oracle reads (the step
+        # never looks at these keys).
+        L = dict(q=q, k=k, v=v, o=wl.sentinel_like(w, DEV), dense=(l == 0), k_ref=k, v_ref=v)
         if l == seqlens_layer:
             L["k"] = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
             L["v"] = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
@@ -150,6 +154,34 @@ def _refresh_inputs(layers, seed):
             D = L["mlp_w1t"].shape[0]
             L["mlp_rows"].copy_(torch.randint(-1, D, L["mlp_rows"].shape, generator=g,
                                               device=DEV, dtype=torch.int32))
+        if "seqlens" in L:
+            n = L["k_ref"].shape[2]
+            L["seqlens"].copy_(torch.randint(0, n + 1, L["seqlens"].shape, generator=g,
+                                             device=DEV, dtype=torch.int32))
+
+
+def _check_oracle(cfg, layers, sentinel_bits):
+    """Each layer's o against the fp64 oracle on the index the step used."""
+    ref_fn = sha_decode_gqa_ref if cfg["gqa"] else sha_decode_ref
+    nh = cfg["H_kv"] if cfg["gqa"] else cfg["H"]
+    for l, L in enumerate(layers):
+        if L["dense"]:
+            idx = np.tile(np.arange(nh, dtype=np.int32), (cfg["B"], 1))
+        else:
+            idx = L["index"].cpu().numpy()
+        sl = L.get("seqlens")
+        O, written = ref_fn(L["q"].cpu(), L["k_ref"].cpu(), L["v_ref"].cpu(), idx, cfg["scale"],
+                            seqlens=None if sl is None else sl.cpu())
+        if L["dense"]:
+            assert written.all()
+        got = L["o"].cpu()
+        g64 = got.double().numpy()
+        assert np.isfinite(g64[written]).all(), f"layer {l}: non-finite active output"
+        err = float(np.max(np.abs(g64[written] - O[written])))
+        assert err <= TOL[cfg["dname"]], f"layer {l}: max abs error {err:.3e}"
+        w = torch.from_numpy(written)
+        assert torch.equal(wl.raw_bits(got)[~w], sentinel_bits[~w]), \
+            f"layer {l}: an unselected slot changed"
 
 
 # (config, MLP (d, D, k per row) or None, layer with per-row lengths, (paged
@@ -180,24 +212,18 @@ def test_step_matches_per_call(case, use_graph):
                           cfg["dtype"], layers, gqa=cfg["gqa"], scale=cfg["scale"],
                           router_d=cfg["router_d"], mlp_d=md, mlp_D=mD, mlp_k=mk,
                           use_graph=use_graph)
+    sentinel_bits = wl.raw_bits(wl.sentinel_like(
+        wl.Workload("s", B=cfg["B"], H=cfg["H"], H_kv=cfg["H_kv"], d=cfg["d"], Nkv=cfg["Nkv"],
+                    top_k=1, dtype=cfg["dname"]), "cpu"))
     try:
         for rep in range(3):
             _reset_outputs(cfg, layers)
             torch.cuda.synchronize()
             step.run()
             torch.cuda.synchronize()
+            _check_oracle(cfg, layers, sentinel_bits)
             ref = _eager(cfg, layers, mlp)
             _compare(layers, ref)
-            if rep == 0:
-                # layer 0 is dense: every head written, equal to the oracle
-                L = layers[0]
-                ref_fn = sha_decode_gqa_ref if cfg["gqa"] else sha_decode_ref
-                nh = cfg["H_kv"] if cfg["gqa"] else cfg["H"]
-                idx = np.tile(np.arange(nh, dtype=np.int32), (cfg["B"], 1))
-                O, written = ref_fn(L["q"].cpu(), L["k"].cpu(), L["v"].cpu(), idx, cfg["scale"])
-                assert written.all()
-                err = float(np.max(np.abs(L["o"].cpu().double().numpy() - O)))
-                assert err <= TOL[cfg["dname"]], err
             # in-place refresh plus unrelated device work before the next run
             _refresh_inputs(layers, seed=100 + rep)
             torch.cuda.synchronize()
@@ -205,3 +231,23 @@ def test_step_matches_per_call(case, use_graph):
             del junk
     finally:
         step.close()
+
+
+def test_step_rejects_tensors_it_would_copy():
+    """The step keeps pointers to its inputs: tensors the binding would have
+    to convert (so that in-place refreshes would never reach the step) are
+    rejected instead."""
+    cfg = dict(CASES["gqa_bf16_ragged"][0])
+    cfg["scale"] = 1.0 / np.sqrt(cfg["d"])
+    layers = _layers(cfg, 2, None, seed=5, seqlens_layer=1)
+    args = (cfg["B"], cfg["H"], cfg["H_kv"], cfg["Nkv"], cfg["d"], cfg["top_k"], cfg["dtype"])
+    kw = dict(gqa=True, scale=cfg["scale"], router_d=cfg["router_d"])
+    bad = [("seqlens", layers[1]["seqlens"].to(torch.int64)),
+           ("index", layers[1]["index"].to(torch.int64)),
+           ("index", layers[1]["index"][:, :1].contiguous()),
+           ("router_scores", layers[1]["router_scores"].to(torch.float16)),
+           ("router_scores", layers[1]["router_scores"].t().contiguous().t())]
+    for name, t in bad:
+        L1 = dict(layers[1], **{name: t})
+        with pytest.raises(ValueError, match=name):
+            sha.DecodeStep(*args, [layers[0], L1], **kw)
