@@ -69,6 +69,7 @@ SIGNATURES = {
     "sha_decode_gqa": (_I, _DECODE_ARGS + [_I]),
     "sha_decode_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
     "sha_decode_gqa_ex": (_I, _DECODE_ARGS + [_I, _I, _P, _S]),
+    "sha_decode_noalloc": (_I, _DECODE_ARGS + [_I, _I, _I]),
     "sha_decode_kv": (_I, _DECODE_ARGS + [_I, _L, _I, _P, _S]),
     "sha_decode_gqa_kv": (_I, _DECODE_ARGS + [_I, _L, _I, _P, _S]),
     "sha_workspace_bytes_kv": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _L]),

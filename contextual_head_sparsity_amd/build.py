@@ -47,7 +47,8 @@ def build(verbose: bool = True) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs, cmds = [], []
-    for src in ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_mlp.hip", "sha_router.hip"):
+    for src in ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_mlp.hip", "sha_router.hip",
+                "sha_noalloc.hip"):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         cmds.append([hipcc, "-c", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS,
                      os.path.join(CSRC, src), "-o", obj])

@@ -162,6 +162,27 @@ sha_status sha_decode_gqa_ex(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes);
 
 /*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * serving loops and harnesses that forbid hipMalloc): sha_decode_ex
+ * (gqa == 0) or sha_decode_gqa_ex (gqa == 1) with the split partials in a
+ * fixed device array of SHA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on, until the process ends, instead of a
+ * caller workspace.  Other arguments and results as those entry points.
+ * The call allocates nothing.  A call whose partials (sha_workspace_bytes
+ * for the same arguments) exceed the array returns SHA_ERR_WORKSPACE and
+ * enqueues nothing.  Every call on one GPU shares that GPU's array and its
+ * kernels overwrite what an earlier call left there (the partials need no
+ * clearing), so calls that may overlap on one GPU (several streams or host
+ * threads) race: order them, or give each its own workspace through
+ * sha_decode_ex.
+ */
+#define SHA_NOALLOC_SCRATCH_BYTES (8u << 20)
+sha_status sha_decode_noalloc(const void* q, const void* k, const void* v,
+                              const int32_t* index, int B, int H, int H_kv, int Nkv, int d,
+                              int top_k, float scale, void* o, hipStream_t stream,
+                              sha_dtype dtype, int gqa, int nsplit);
+
+/*
  * KV cache layouts and per-row cache lengths.  A decode batch mixes requests
  * whose caches hold different numbers of keys, and serving stacks keep the
  * cache as [B, Nkv, H_kv, d], as per-head slabs, or in fixed-size pages.

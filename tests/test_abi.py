@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
