@@ -34,7 +34,11 @@ from contextual_head_sparsity_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E peak, GB/s
 CSRC = os.path.join(ROOT, "contextual_head_sparsity_amd", "csrc")
-KERNEL_SOURCES = ("sha_kernels.hip", "sha_gqa_mfma.hip", "sha_device.h", "sha_decode.h")
+# Sources of each decode kernel: its own file plus the shared device headers.
+KERNEL_SOURCES = {False: ("sha_kernels.hip", "sha_device.h", "sha_decode.h"),
+                  True: ("sha_gqa_mfma.hip", "sha_device.h", "sha_decode.h")}
+# The density sweep at the OPT-66B shape: active heads out of 72 per row.
+SWEEP_TOP_K = (7, 14, 22, 36, 54, 72)
 METRIC = "SHA decode \u00b5s/layer + effective KV GB/s (% HBM peak), OPT-66B shape B=64"
 
 
@@ -47,11 +51,11 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_hash() -> str:
-    """Hash of the decode kernels' sources (code only): counter-derived
-    traffic is only reported for the kernels it was measured on."""
+def kernel_hash(gqa: bool) -> str:
+    """Hash of one decode kernel's sources (code only): counter-derived
+    traffic is only reported for the kernel it was measured on."""
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[bool(gqa)]:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -71,6 +75,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-workload block and the density sweep (headline only)")
+    p.add_argument("--sweep-out", default=None,
+                   help="also write the density sweep to this JSON file")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calib", action="store_true")
     p.add_argument("--summarize-traffic", action="store_true",
@@ -160,6 +168,123 @@ def read_probe(dev, nbytes: int = 1 << 31):
             "kernel": "sha_probe_read_kernel (libsha_probe.so)"}
 
 
+def rotating_kv(w, dev, k, v, copies=0):
+    """K/V copies that consecutive calls rotate through, so that neither the
+    4 MB L2 per XCD nor the 256 MB MALL can serve a call from the last one
+    (at most 256 copies: the tiny workload stays launch-bound anyway)."""
+    copies = copies or min(256, max(2, math.ceil(2 * 256e6 / w.active_kv_bytes)))
+    ks, vs = [k], [v]
+    for c in range(1, copies):
+        _, kc, vc = wl.make_qkv(w, dev, seed_offset=c)
+        ks.append(kc)
+        vs.append(vc)
+    return ks, vs, copies
+
+
+def decode_timing(w, q, ks, vs, index, nsplit, steps, warmup, stream):
+    """(wall ms per call, per-launch event ms) of back-to-back decode calls
+    over the rotating K/V copies, with a workspace allocated up front."""
+    fn = sha.sha_decode_gqa if w.gqa else sha.sha_decode
+    top_k = index.shape[1]
+    wsb = sha.workspace_bytes(w.B, w.H, w.H_kv, w.Nkv, w.d, top_k, w.gqa, q.dtype, nsplit)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
+    out = torch.zeros_like(q)
+    n = len(ks)
+
+    def call(i):
+        fn(q, ks[i % n], vs[i % n], index, scale=w.scale, out=out, nsplit=nsplit, workspace=ws,
+           stream=stream)
+
+    return time_calls(call, steps, warmup, stream)
+
+
+def selected_mask(w, idx_cpu):
+    G = w.H // w.H_kv
+    sel = torch.zeros(w.B, w.H, dtype=torch.bool)
+    for b in range(w.B):
+        for e in idx_cpu[b]:
+            if w.gqa and 0 <= e < w.H_kv:
+                sel[b, e * G:(e + 1) * G] = True
+            elif not w.gqa and 0 <= e < w.H:
+                sel[b, e] = True
+    return sel
+
+
+def output_check(w, q, k, v, idx, dev):
+    """One call into a sentinel-filled output: unselected slots keep their
+    bits, selected ones are finite."""
+    fn = sha.sha_decode_gqa if w.gqa else sha.sha_decode
+    o_chk = wl.sentinel_like(w, dev)
+    fn(q, k, v, idx, scale=w.scale, out=o_chk)
+    torch.cuda.synchronize()
+    sel = selected_mask(w, idx.cpu().numpy()).to(dev)
+    return o_chk, {"active_slots": int(sel.sum()),
+                   "unselected_bits_untouched": bool(torch.equal(
+                       wl.raw_bits(o_chk)[~sel], wl.raw_bits(wl.sentinel_like(w, dev))[~sel])),
+                   "selected_finite": bool(torch.isfinite(o_chk[sel]).all())}
+
+
+def config_entry(w, dev, steps, warmup, stream):
+    """Per-workload summary: µs per layer call, effective KV GB/s and % of
+    peak (wall time over back-to-back calls), roofline fraction from the
+    per-launch event durations, planned split count, and the speedup over the
+    same kernel with every head (group) active."""
+    q, k, v, idx, _ = wl.make_workload(w, dev)
+    ks, vs, copies = rotating_kv(w, dev, k, v)
+    ns = sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa, q.dtype)
+    ms, ev = decode_timing(w, q, ks, vs, idx, ns, steps, warmup, stream)
+    n_sel = w.H_kv if w.gqa else w.H
+    dense_idx = torch.arange(n_sel, dtype=torch.int32, device=dev).repeat(w.B, 1)
+    dn = sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, n_sel, w.gqa, q.dtype)
+    dms, _ = decode_timing(w, q, ks, vs, dense_idx, dn, max(steps // 2, 5), max(warmup // 2, 2),
+                           stream)
+    _, check = output_check(w, q, k, v, idx, dev)
+    ev_ms = float(np.mean(ev))
+    gbs = w.active_kv_bytes / (ms / 1e3) / 1e9
+    entry = {"B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d, "Nkv": w.Nkv, "top_k": w.top_k,
+             "gqa": w.gqa, "dtype": w.dtype, "index_sampling": w.sampling,
+             "active_kv_bytes": w.active_kv_bytes, "nsplit": ns, "kv_copies_rotated": copies,
+             "us_per_layer": round(ms * 1e3, 2), "kv_GBps": round(gbs, 1),
+             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+             "launch_avg_us": round(ev_ms * 1e3, 2),
+             "roofline_frac": round(w.active_kv_bytes / (ev_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+             "all_heads_us": round(dms * 1e3, 2), "all_heads_nsplit": dn,
+             "speedup_vs_all_heads": round(dms / ms, 3),
+             "ideal_speedup": round(n_sel / w.top_k, 3), "check": check}
+    if w.units < 64:
+        entry["note"] = "launch-bound (a few KB per call): a parity case, not a bandwidth one"
+    del q, k, v, ks, vs
+    torch.cuda.empty_cache()
+    return entry
+
+
+def density_sweep(w, q, ks, vs, dev, steps, warmup, stream):
+    """The same layer with top_k of the H heads active, for each top_k in
+    SWEEP_TOP_K (index rows drawn like the workload's), against all heads
+    active: speedup vs the ideal H / top_k (near-linear sparsity-to-speedup
+    is the pages' claim for the attention kernel)."""
+    pts = {}
+    for k_act in SWEEP_TOP_K:
+        wk = w.with_(top_k=k_act)
+        idx = torch.from_numpy(wl.sample_index(wk)).to(dev)
+        ns = sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, k_act, w.gqa, q.dtype)
+        ms, ev = decode_timing(wk, q, ks, vs, idx, ns, steps, warmup, stream)
+        pts[k_act] = (ms, float(np.mean(ev)), ns, wk.active_kv_bytes)
+    t_all = pts[max(SWEEP_TOP_K)][0]
+    n_sel = w.H_kv if w.gqa else w.H
+    points = []
+    for k_act, (ms, ev_ms, ns, nbytes) in pts.items():
+        sp = t_all / ms
+        points.append({"top_k": k_act, "density": round(k_act / n_sel, 4), "nsplit": ns,
+                       "us_per_layer": round(ms * 1e3, 2),
+                       "kv_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+                       "launch_avg_us": round(ev_ms * 1e3, 2),
+                       "speedup_vs_all_heads": round(sp, 3),
+                       "ideal_speedup": round(n_sel / k_act, 3),
+                       "efficiency": round(sp * k_act / n_sel, 3)})
+    return {"workload": w.name, "all_heads_top_k": max(SWEEP_TOP_K), "points": points}
+
+
 ORACLE_TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}   # max abs error, N(0, 1) inputs
 
 
@@ -224,7 +349,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256_16") != kernel_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_hash(wl.WORKLOADS[workload].gqa):
         return None   # counters were taken on an older kernel
     return rec.get("hbm_bytes_per_launch")
 
@@ -263,7 +388,7 @@ def summarize_traffic(args):
     write_scale = copy_bytes / (w_cp * 1024)
     read_b = f_dec * 1024 * fetch_scale
     write_b = w_dec * 1024 * write_scale
-    rec = {"workload": w.name, "kernel": kname, "kernel_source_sha256_16": kernel_hash(),
+    rec = {"workload": w.name, "kernel": kname, "kernel_source_sha256_16": kernel_hash(w.gqa),
            "dispatches": {"fetch": nf, "write": nw},
            "fetch_size_kib_per_launch": f_dec, "write_size_kib_per_launch": w_dec,
            "copy_1GiB_fetch_kib": f_cp, "copy_1GiB_write_kib": w_cp,
@@ -499,14 +624,7 @@ def main():
     dev = torch.device("cuda:0")
     fn = sha.sha_decode_gqa if w.gqa else sha.sha_decode
     q, k, v, idx, o = wl.make_workload(w, dev)
-    # Rotating K/V copies: consecutive steps read disjoint memory, so neither
-    # the 4 MB L2 per XCD nor the 256 MB MALL can serve a step from the last.
-    copies = args.copies or max(2, math.ceil(2 * 256e6 / w.active_kv_bytes))
-    ks, vs = [k], [v]
-    for c in range(1, copies):
-        _, kc, vc = wl.make_qkv(w, dev, seed_offset=c)
-        ks.append(kc)
-        vs.append(vc)
+    ks, vs, copies = rotating_kv(w, dev, k, v, args.copies)
     nsplit = args.nsplit or sha.plan_nsplit(w.B, w.H, w.H_kv, w.Nkv, w.d, w.top_k, w.gqa,
                                             q.dtype)
     layout = args.kv_layout
@@ -599,28 +717,44 @@ def main():
     # One more call, outside the timed region, into a fresh sentinel-filled
     # output on the first K/V copy: unselected slots must keep their bits and
     # selected ones must be finite (the oracle leg below also compares them).
-    o_chk = wl.sentinel_like(w, dev)
-    call(0, out=o_chk)
-    torch.cuda.synchronize()
-    idx_cpu = idx.cpu().numpy()
-    G = w.H // w.H_kv
-    sel = torch.zeros(w.B, w.H, dtype=torch.bool)
-    for b in range(w.B):
-        for e in idx_cpu[b]:
-            if w.gqa and 0 <= e < w.H_kv:
-                sel[b, e * G:(e + 1) * G] = True
-            elif not w.gqa and 0 <= e < w.H:
-                sel[b, e] = True
-    sel = sel.to(dev)
-    out["check"] = {"active_slots": int(sel.sum()),
-                    "unselected_bits_untouched": bool(torch.equal(
-                        wl.raw_bits(o_chk)[~sel], wl.raw_bits(wl.sentinel_like(w, dev))[~sel])),
-                    "selected_finite": bool(torch.isfinite(o_chk[sel]).all())}
+    if page:
+        o_chk = wl.sentinel_like(w, dev)
+        call(0, out=o_chk)
+        torch.cuda.synchronize()
+        sel = selected_mask(w, idx.cpu().numpy()).to(dev)
+        out["check"] = {"active_slots": int(sel.sum()),
+                        "unselected_bits_untouched": bool(torch.equal(
+                            wl.raw_bits(o_chk)[~sel], wl.raw_bits(wl.sentinel_like(w, dev))[~sel])),
+                        "selected_finite": bool(torch.isfinite(o_chk[sel]).all())}
+    else:
+        o_chk, out["check"] = output_check(w, q, ks[0], vs[0], idx, dev)
     probe = read_probe(dev) if not args.no_probe else None
     out["read_probe"] = probe
     out["pct_of_read_probe"] = round(100 * value / probe["GBps"], 2) if probe else None
     if not args.no_cpu_baseline and layout == "contig":
         out["cpu_baseline"] = cpu_baseline(w, q, ks[0], vs[0], idx, args.cpu_seconds, o_gpu=o_chk)
+    if not args.no_configs and layout == "contig" and w.name == wl.HEADLINE:
+        csteps, cwarm = min(args.steps, 30), min(args.warmup, 5)
+        sweep = density_sweep(w, q, ks, vs, dev, csteps, cwarm, stream)
+        out["density_sweep"] = sweep
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                json.dump(sweep, f, indent=1)
+        entries = {w.name: {"us_per_layer": out["us_per_layer"],
+                            "kv_GBps": out["value"], "pct_hbm_peak": out["pct_hbm_peak"],
+                            "launch_avg_us": out["roofline"]["launch_avg_us"],
+                            "roofline_frac": out["roofline"]["frac"], "nsplit": nsplit,
+                            "all_heads_us": dense and round(dense["us_per_layer"], 2),
+                            "speedup_vs_all_heads": dense and round(
+                                dense["speedup_sparse_vs_all_heads"], 3),
+                            "ideal_speedup": dense and round(dense["ideal_speedup"], 3),
+                            "check": out["check"], "note": "the headline measurement above"}}
+        del q, k, v, ks, vs, o_chk
+        torch.cuda.empty_cache()
+        for name, wc in wl.WORKLOADS.items():
+            if name != w.name:
+                entries[name] = config_entry(wc, dev, csteps, cwarm, stream)
+        out["configs"] = {n: entries[n] for n in wl.WORKLOADS}
     print(json.dumps(out), flush=True)
 
 

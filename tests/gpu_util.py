@@ -126,3 +126,50 @@ def paged(w, k, v, P, pool="nphd", seed=0, extra=3):
     if pool == "nphd":
         kd, vd = kd.permute(0, 2, 1, 3), vd.permute(0, 2, 1, 3)
     return kd, vd, torch.from_numpy(bt).to(DEV)
+
+
+def check_every_slot(gqa, q, k, v, idx, scale, o_before_bits, o_after, tol):
+    """Full-size comparison of every active slot, one batch row at a time so
+    that host memory holds one row's selected K/V: the row's selected heads
+    (or groups, with their G query heads) are gathered on the device into a
+    compact problem with index 0 .. top_k-1 and run through the whole-call
+    oracle; plus whole-tensor properties (inactive slots bit-identical to
+    their prefill, active slots finite).  Returns (max abs error, slots)."""
+    B, H = q.shape[:2]
+    H_kv = k.shape[1]
+    G = H // H_kv
+    idx_cpu = idx.cpu().numpy()
+    w = written_mask(idx_cpu, H, H_kv, gqa)
+    wt = torch.from_numpy(w).to(o_after.device)
+    assert torch.equal(wl.raw_bits(o_after)[~wt], o_before_bits[~wt]), "an inactive slot changed"
+    assert torch.isfinite(o_after[wt]).all(), "non-finite output in an active slot"
+    err, slots = 0.0, 0
+    for b in range(B):
+        sel = [int(e) for e in idx_cpu[b] if 0 <= e < (H_kv if gqa else H)]
+        if not sel:
+            continue
+        if gqa:
+            heads = [g * G + j for g in sel for j in range(G)]
+            kv_rows = sel
+        else:
+            heads = sel
+            kv_rows = [h // G for h in sel]
+        dev_h = torch.tensor(heads, device=q.device)
+        dev_g = torch.tensor(kv_rows, device=q.device)
+        qc = q[b].index_select(0, dev_h).unsqueeze(0).cpu()         # [1, n_heads, 1, d]
+        kc = k[b].index_select(0, dev_g).unsqueeze(0).cpu()         # [1, n_kv, Nkv, d]
+        vc = v[b].index_select(0, dev_g).unsqueeze(0).cpu()
+        if gqa:
+            compact = np.arange(len(sel), dtype=np.int32)[None, :]
+            ref, written = sha_decode_gqa_ref(qc, kc, vc, compact, scale)
+        else:
+            # head j of the compact problem reads KV row j (H_kv = H there)
+            compact = np.arange(len(sel), dtype=np.int32)[None, :]
+            ref, written = sha_decode_ref(qc, kc, vc, compact, scale)
+        assert written.all()
+        got = o_after[b].index_select(0, dev_h).cpu().to(torch.float64).numpy()
+        err = max(err, float(np.max(np.abs(got - ref[0]))))
+        slots += len(set(heads))
+    assert err <= tol, f"max abs error {err:.3e} > {tol}"
+    assert slots == int(w.sum())
+    return err, slots
