@@ -411,7 +411,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
 // selective MLP planning
 // ---------------------------------------------------------------------------
 struct MlpPlan {
-  int n_pad, b_pad, up_splits, up_kper, dn_splits;
+  int n_pad, b_pad, bb, up_splits, up_kper, dn_splits;
   size_t h_bytes, up_bytes, dn_bytes;
 };
 
@@ -427,7 +427,6 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 //         neurons, at most 64 splits).
 // The constants come from split sweeps of the OPT MLPs on MI355X.
 constexpr int kUpWgsPerCu = 2;
-constexpr int kMaxUpSplits = 8;
 constexpr int kDownWgsPerCu = 2;
 
 int up_split_count(long long items, int kstages, int cus) {
@@ -436,7 +435,7 @@ int up_split_count(long long items, int kstages, int cus) {
   // a grid already past that takes no splits beyond it.
   const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
   long long us = (slots * 95 / 100 + items - 1) / items;
-  if (us > kMaxUpSplits) us = kMaxUpSplits;
+  if (us > sha::kMlpMaxUpSplits) us = sha::kMlpMaxUpSplits;
   if (us > kstages) us = kstages;
   return us < 1 ? 1 : static_cast<int>(us);
 }
@@ -447,10 +446,12 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   constexpr int NU = sha::kMlpUpNeurons;
   p.n_pad = ((n_max > 0 ? n_max : 1) + NU - 1) / NU * NU;
   p.b_pad = (B + 63) / 64 * 64;
+  p.bb = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
   const long long up_items = static_cast<long long>(p.n_pad / NU) * (p.b_pad / 64);
   const int kstages = d / sha::kMlpUpKc;
   int us = up_split_count(up_items, kstages, cus);
   if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
+  if (us > sha::kMlpMaxUpSplits) us = sha::kMlpMaxUpSplits;
   if (us > kstages) us = kstages;
   p.up_kper = (kstages + us - 1) / us * sha::kMlpUpKc;
   p.up_splits = (d + p.up_kper - 1) / p.up_kper;
@@ -690,6 +691,7 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.n_max = n_max;
   a.n_pad = p.n_pad;
   a.b_pad = p.b_pad;
+  a.bb = p.bb;
   a.up_splits = p.up_splits;
   a.up_kper = p.up_kper;
   a.dn_splits = p.dn_splits;

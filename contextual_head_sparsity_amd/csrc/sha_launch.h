@@ -17,6 +17,7 @@ namespace sha {
 // workgroup, in K stages of kMlpUpKc.
 constexpr int kMlpUpNeurons = 128;
 constexpr int kMlpUpKc = 128;
+constexpr int kMlpMaxUpSplits = 8;     // K splits of the up projection (at most)
 struct MlpArgs {
   const void* x;        // [B, d]
   const void* w1t;      // [D, d]  (W1^T, neuron-major)
@@ -29,6 +30,9 @@ struct MlpArgs {
   float* dn_part;       // workspace: down-projection split partials [dn_splits, b_pad, d]
   int B, d, D, n_max;
   int n_pad, b_pad;     // n_max rounded up to kMlpUpNeurons, B rounded up to 64
+  int bb;               // 16-row batch blocks computed per 64-row tile: 1 (B <= 16),
+                        // 2 (B <= 32) or 4; rows 16 bb .. 63 of a tile are never
+                        // computed, read for an output row, or stored
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
 };

@@ -232,9 +232,15 @@ struct UpX {
   uint4 v[kUpX];
 };
 
-template <int DT>
+// BB = 16-row batch blocks computed per 64-row tile (1 for B <= 16, 2 for
+// B <= 32, else 4).  The four waves split the tile's 8 neuron blocks into
+// 4 / BB groups: wave w multiplies neuron blocks of group w / BB by batch
+// block w % BB, so no wave multiplies padding rows of a small batch.
+template <int DT, int BB>
 __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
+  static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
+  constexpr int NBW = kUpNB * BB / 4;         // neuron blocks per wave
   __shared__ __attribute__((aligned(16))) char wsm_[2 * kUpN * kUpRowB];
   const int nblocks = a.n_pad / kUpN;
   int t = blockIdx.x;
@@ -272,14 +278,16 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   // are finite and no output row reads them (the down projection stores only
   // rows < B), so x is not masked (a mask applied to freshly loaded x made
   // the wave wait for the weight loads in flight before it).
-  const int b = b0 + 16 * wave + c;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wu / BB;                    // neuron blocks grp * NBW .. + NBW - 1
+  const int b = b0 + 16 * (wu % BB) + c;
   const bool xok = b < a.B;
   const char* xsrc = static_cast<const char*>(a.x) +
                      (static_cast<size_t>(xok ? b : a.B - 1) * a.d + kbeg + 8 * q4) * 2;
 
-  f32x4 acc[kUpNB];  // [neuron block]; batch block = wave
+  f32x4 acc[NBW];  // [neuron block of the group]; batch block = wave % BB
 #pragma unroll
-  for (int i = 0; i < kUpNB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NBW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto load_w = [&](int st, UpW& d) {
 #pragma unroll
@@ -316,9 +324,10 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
       const uint4 xb = xv;
       const int piece = 4 * s + q4;         // 16-byte piece of the row this lane reads
 #pragma unroll
-      for (int mb = 0; mb < kUpNB; ++mb) {
+      for (int i = 0; i < NBW; ++i) {
+        const int mb = grp * NBW + i;
         const u32x4_t av = *(const lds_u32x4_t*)(buf + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
-        acc[mb] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[mb]);
+        acc[i] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[i]);
       }
     }
     __syncthreads();
@@ -353,42 +362,53 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
     if (st < nst) step(st, wb, x0, x1, Chk{});
   }
 
-  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] (b < b_pad)
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b]: the computed rows of the
+  // tile (16 BB of its 64).
 #pragma unroll
-  for (int mb = 0; mb < kUpNB; ++mb) {
-    const int nbase = n0 + 16 * mb + 4 * q4;
+  for (int i = 0; i < NBW; ++i) {
+    const int nbase = n0 + 16 * (grp * NBW + i) + 4 * q4;
     // Entries outside [0, D) (and past the count) produce no activation.
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (!sel_valid(a, nbase + r, n_sel)) acc[mb][r] = 0.f;
+      if (!sel_valid(a, nbase + r, n_sel)) acc[i][r] = 0.f;
     if (a.up_splits == 1) {
-      const uint32_t lo = M::pack(fmaxf(acc[mb][0], 0.f), fmaxf(acc[mb][1], 0.f));
-      const uint32_t hi = M::pack(fmaxf(acc[mb][2], 0.f), fmaxf(acc[mb][3], 0.f));
+      const uint32_t lo = M::pack(fmaxf(acc[i][0], 0.f), fmaxf(acc[i][1], 0.f));
+      const uint32_t hi = M::pack(fmaxf(acc[i][2], 0.f), fmaxf(acc[i][3], 0.f));
       *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
                                 (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
     } else {
       float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
-      *reinterpret_cast<float4*>(p) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+      *reinterpret_cast<float4*>(p) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     }
   }
 }
 
-// H = relu(sum of the K-split partials), fixed order; one thread per 4 neurons.
+// H = relu(sum of the K-split partials), fixed order; one thread per 4
+// neurons of a computed row (rows 16 bb of each 64-row tile).  The splits'
+// loads are issued together (at most kMlpMaxUpSplits), then summed in order.
 template <int DT>
 __global__ __launch_bounds__(256) void sha_mlp_up_finalize_kernel(MlpArgs a) {
   using M = Mx<DT>;
   const int n_sel = sel_count(a);
-  const size_t quads = static_cast<size_t>(a.b_pad) * (a.n_pad / 4);
+  const int rows = 16 * a.bb;                  // computed rows per tile
+  const size_t quads = static_cast<size_t>(a.b_pad / 64) * rows * (a.n_pad / 4);
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < quads; i += static_cast<size_t>(gridDim.x) * 256) {
-    const size_t b = i / (a.n_pad / 4);
+    const size_t rq = i / (a.n_pad / 4);
+    const size_t b = (rq / rows) * 64 + rq % rows;
     const int n4 = static_cast<int>(i % (a.n_pad / 4)) * 4;
     if (n4 >= n_sel) continue;
+    float4 v[kMlpMaxUpSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMlpMaxUpSplits; ++sp)
+      if (sp < a.up_splits)
+        v[sp] = *reinterpret_cast<const float4*>(
+            a.up_part + (static_cast<size_t>(sp) * a.b_pad + b) * a.n_pad + n4);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < a.up_splits; ++sp) {
-      const float4 v = *reinterpret_cast<const float4*>(
-          a.up_part + (static_cast<size_t>(sp) * a.b_pad + b) * a.n_pad + n4);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
+#pragma unroll
+    for (int sp = 0; sp < kMlpMaxUpSplits; ++sp)
+      if (sp < a.up_splits) {
+        s.x += v[sp].x; s.y += v[sp].y; s.z += v[sp].z; s.w += v[sp].w;
+      }
     const uint32_t lo = M::pack(fmaxf(s.x, 0.f), fmaxf(s.y, 0.f));
     const uint32_t hi = M::pack(fmaxf(s.z, 0.f), fmaxf(s.w, 0.f));
     *reinterpret_cast<uint2*>(static_cast<char*>(a.h) + (b * a.n_pad + n4) * 2) = make_uint2(lo, hi);
@@ -405,10 +425,14 @@ constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 B: conflict-free transposed r
 constexpr int kDnHPitch = kDnKc * 2 + 16;   // 144 B: conflict-free H reads
 
 // Two workgroups per CU (the planner's assumption): the register budget is
-// held at 256 per lane, accumulators included.
-template <int DT>
+// held at 256 per lane, accumulators included.  BB = 16-row batch blocks
+// computed per 64-row tile (as in the up projection): only those rows of H
+// are loaded and multiplied.
+template <int DT, int BB>
 __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   using M = Mx<DT>;
+  static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
+  constexpr int HL = BB == 4 ? 2 : 1;         // H pieces per thread (32 rows each)
   __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
   __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
   const int n_sel = sel_count(a);
@@ -436,15 +460,15 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   lds_char_t* const wl = (lds_char_t*)(ws_);
   lds_char_t* const hl = (lds_char_t*)(hs_);
 
-  f32x4 acc[4][4];  // [m block (batch)][n block (columns)]
+  f32x4 acc[BB][4];  // [m block (batch)][n block (columns)]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Gathered W2t rows of a chunk: 64 rows x 512 B = 2048 pieces (8 per
-  // thread); H chunk: 64 rows x 128 B = 512 pieces (2 per thread), neurons at
-  // or past nend read as zero.  Piece tid + 256 i of the weights is row
+  // thread); H chunk: 32 HL rows x 128 B = 256 HL pieces (HL per thread; at
+  // least the 16 BB computed rows), neurons at or past nend read as zero.  Piece tid + 256 i of the weights is row
   // 2 wave + (lane >> 5) + 8 i, so each load instruction needs two selection
   // entries that are the same for the whole wave: they are read with scalar
   // loads (own counter), and the vector loads of earlier chunks need not
@@ -454,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   // for them, and (loads complete in order) for every older load, at once.
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const bool upper = lane >= 32;
-  auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[2]) {
+  auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[HL]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r0 = k0 + 2 * wu + 8 * i;
@@ -465,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
                           (static_cast<size_t>(row) * a.d + col0 + (lane & 31) * 8) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < HL; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, piece = idx & 7;
       const int nc = min(k0 + piece * 8, a.n_pad - 8);  // past n_pad: past nend, masked
@@ -479,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   // set with chunk j + 2 (two chunks in flight during the products), publish
   // and multiply.  CHECK: only load inside the range.
   const int nch = nend > nbeg ? (nend - nbeg + kDnKc - 1) / kDnKc : 0;
-  auto step = [&](int j, uint4 (&w)[8], uint4 (&h)[2], auto check) {
+  auto step = [&](int j, uint4 (&w)[8], uint4 (&h)[HL], auto check) {
     constexpr bool C = decltype(check)::value;
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
@@ -489,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
       *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, w[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < HL; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 3, piece = idx & 7;
       const int cnt = min(max(nend - (nbeg + j * kDnKc + piece * 8), 0), 8);  // valid neurons
@@ -509,9 +533,9 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
     for (int ks = 0; ks < kDnKc / 32; ++ks) {
       // K-slot order of a 32-neuron step: lane group q4 owns neurons
       // 4q4 .. 4q4+3 and 16+4q4 .. 16+4q4+3 of the step.
-      uint4 ha[4];
+      uint4 ha[BB];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < BB; ++mb) {
         const lds_char_t* hr = hl + (16 * mb + c) * kDnHPitch + ks * 64;
         const u32x2_t p0 = *(const lds_u32x2_t*)(hr + 8 * q4);
         const u32x2_t p1 = *(const lds_u32x2_t*)(hr + 32 + 8 * q4);
@@ -525,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
         const uint2 x1 = M::tr_read(wl + (trow + 16) * kDnWPitch + cb);
         const uint4 wb = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[mb][nb] = M::mma(ha[mb], wb, acc[mb][nb]);
+        for (int mb = 0; mb < BB; ++mb) acc[mb][nb] = M::mma(ha[mb], wb, acc[mb][nb]);
       }
     }
   };
@@ -536,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
     // at the loop head from the entry and from the back edge and can leave
     // the younger set in flight; a conditional second load makes it wait
     // for everything there.
-    uint4 wa[8], ha0[2], wb8[8], hb0[2];
+    uint4 wa[8], ha0[HL], wb8[8], hb0[HL];
     load_chunk(nbeg, wa, ha0);
     load_chunk(nbeg + min(1, nch - 1) * kDnKc, wb8, hb0);
     using Chk = std::true_type;
@@ -555,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
 
   // lane holds y[b = b0 + 16 mb + 4 q4 + r][col = col0 + 64 wave + 16 nb + c]
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < BB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int b = b0 + 16 * mb + 4 * q4 + r;
@@ -572,7 +596,8 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
 }
 
 // y = sum of the neuron-split partials, fixed order; one thread per 4
-// consecutive columns (d is a multiple of 256).
+// consecutive columns (d is a multiple of 256).  Loads of eight splits are
+// issued together, then summed in order.
 template <int DT>
 __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
   const size_t quads = static_cast<size_t>(a.B) * (a.d / 4);
@@ -580,9 +605,16 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < quads; i += static_cast<size_t>(gridDim.x) * 256) {
     const float4* p = reinterpret_cast<const float4*>(a.dn_part) + i;  // row-major [b][d] of plane 0
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < a.dn_splits; ++sp) {
-      const float4 v = p[sp * (plane / 4)];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    for (int sp0 = 0; sp0 < a.dn_splits; sp0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < a.dn_splits) v[u] = p[(sp0 + u) * (plane / 4)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < a.dn_splits) {
+          s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+        }
     }
     const size_t e = i * 4;
     Elem<DT>::store(a.y, e, s.x);
@@ -592,23 +624,23 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
   }
 }
 
-template <int DT>
-hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
+template <int DT, int BB>
+hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
   const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
-  hipLaunchKernelGGL((sha_mlp_up_kernel<DT>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
+  hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
                      st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.up_splits > 1) {
-    const size_t quads = static_cast<size_t>(a.b_pad) * (a.n_pad / 4);
+    const size_t quads = static_cast<size_t>(btiles) * 16 * BB * (a.n_pad / 4);
     const unsigned blocks = static_cast<unsigned>(quads < 256 * 1024 ? (quads + 255) / 256 : 1024);
     hipLaunchKernelGGL((sha_mlp_up_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 1-D over (column block, split, batch tile): the kernel maps the ids
   // onto XCDs itself.
-  hipLaunchKernelGGL((sha_mlp_down_kernel<DT>),
+  hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB>),
                      dim3(static_cast<unsigned>((a.d / kDnCols) * a.dn_splits) * btiles),
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -619,6 +651,16 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
     e = hipGetLastError();
   }
   return e;
+}
+
+template <int DT>
+hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
+  switch (a.bb) {
+    case 1: return launch_mlp_bb<DT, 1>(a, st);
+    case 2: return launch_mlp_bb<DT, 2>(a, st);
+    case 4: return launch_mlp_bb<DT, 4>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

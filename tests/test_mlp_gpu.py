@@ -69,9 +69,13 @@ def test_union_rows_not_16_byte_aligned():
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("B,d,D,k_row", [(1, 256, 300, 20), (3, 256, 1000, 50), (64, 512, 2000, 100),
-                                         (70, 256, 700, 30), (5, 768, 4096, 400)])
+                                         (70, 256, 700, 30), (5, 768, 4096, 400),
+                                         (17, 256, 800, 40), (20, 256, 1500, 60),
+                                         (32, 512, 2500, 80), (40, 256, 900, 50)])
 def test_selective_mlp_union_pipeline(dtype, B, d, D, k_row):
-    """router rows -> union on device -> selective MLP; compare with the oracle."""
+    """router rows -> union on device -> selective MLP; compare with the oracle.
+    Batches of 1-16, 17-32 and 33+ rows run the kernels' 1, 2 and 4 batch-block
+    forms (70 rows: two batch tiles)."""
     say(f"[mlp] pipeline {dtype} B={B} d={d} D={D} k_row={k_row}")
     w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype=dtype, seed=B + d)
     x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
