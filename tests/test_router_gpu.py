@@ -123,3 +123,60 @@ def test_group_router_feeds_gqa_decode():
     ref, written = sha_decode_gqa_ref(q, k, v, gidx.cpu(), w_.scale)
     g = od.cpu().double().numpy()
     assert float(np.abs(g[written] - ref[written]).max()) <= 1e-2
+
+
+def test_router_consecutive_calls_and_streams():
+    """Consecutive calls of growing and shrinking batches and widths, on the
+    current stream and on a side stream, all match the oracle."""
+    side = torch.cuda.Stream(device=DEV)
+    for i, (B, d, H, k, st) in enumerate([(3, 256, 72, 22, None), (5000, 128, 72, 22, None),
+                                          (64, 9216, 72, 22, None), (7, 512, 40, 8, side),
+                                          (4100, 64, 13, 4, side), (3, 12288, 9, 4, side),
+                                          (2, 64, 8, 3, None)]):
+        say(f"[router] counters call {i}: B={B} d={d} H={H} k={k} side={st is not None}")
+        x, w, b = _inputs(B, d, H, "bf16", seed=100 + i)
+        xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+        if st is not None:
+            st.wait_stream(torch.cuda.current_stream())
+        idx, sc = sha.router_topk(xd, wd, k, bias=bd, stream=st)
+        torch.cuda.synchronize()
+        _check(x, w, b, k, idx, sc)
+
+
+@pytest.mark.parametrize("warm", [False, True])
+def test_router_graph_replays(warm):
+    """A router call captured in a graph, on a fresh or an already used
+    stream: each replay (with eager router calls on the same stream in
+    between) matches the eager result bit for bit and the oracle."""
+    say(f"[router] graph replays warm={warm}")
+    B, d, H, k = 48, 2048, 72, 22
+    x, w, b = _inputs(B, d, H, "f16", seed=7)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    sc = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    if warm:
+        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s)
+        s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s)
+    torch.cuda.synchronize()
+    x2, w2, b2 = _inputs(B, d, H, "f16", seed=8)
+    eager_idx, eager_sc = None, None
+    for rep in range(3):
+        idx.fill_(-1)
+        sc.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _check(x, w, b, k, idx, sc)
+        if eager_idx is None:
+            eager_idx, eager_sc = sha.router_topk(xd, wd, k, bias=bd, stream=s)
+            s.synchronize()
+        assert torch.equal(idx, eager_idx) and torch.equal(sc, eager_sc)
+        # other work on the captured stream between replays
+        i2, s2 = sha.router_topk(x2.to(DEV), w2.to(DEV), k, bias=b2.to(DEV), stream=s)
+        s.synchronize()
+        _check(x2, w2, b2, k, i2, s2)
