@@ -93,6 +93,8 @@ def parse():
     p.add_argument("--mlp", default=None, choices=list(wl.MLP_WORKLOADS),
                    help="measure the selective MLP on this workload instead of SHA decode")
     p.add_argument("--mlp-batch", type=int, default=0, help="override the MLP workload's B")
+    p.add_argument("--mlp-sweep", action="store_true",
+                   help="with --mlp: time batches 1, 2, 4, ..., B (union density sweep)")
     p.add_argument("--decode-step", type=int, default=0, metavar="L",
                    help="time an L-layer decode step (router -> SHA -> selective MLP, layer 0 "
                         "dense) as one HIP graph and call by call")
@@ -462,6 +464,67 @@ def bench_mlp(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_mlp_sweep(args):
+    """Selective MLP speedup against the all-neurons call as the batch union
+    grows: batches 1, 2, 4, ... up to the workload's B on one set of weights
+    (x = the first B rows, each row's neurons the workload's seeded draw, so
+    a smaller batch's rows are a prefix of a larger one's).  Per point: union
+    size, µs per selective call (device union + MLP), µs per all-neurons call,
+    speedup and its ideal D / |union|."""
+    w = wl.MLP_WORKLOADS[args.mlp]
+    dev = torch.device("cuda:0")
+    x, w1t, w2t, rows = wl.make_mlp(w, dev)
+    ws = [(w1t, w2t), (torch.roll(w1t, 1, 0).contiguous(), torch.roll(w2t, 1, 0).contiguous())]
+    stream = torch.cuda.current_stream(dev)
+    sel_all = torch.arange(w.D, dtype=torch.int32, device=dev)
+    n_all = torch.tensor([w.D], dtype=torch.int32, device=dev)
+    uws = torch.empty(sha.lib().sha_mlp_union_workspace_bytes(w.D), dtype=torch.uint8, device=dev)
+    points = []
+    B = 1
+    while B <= w.B:
+        xb = x[:B].contiguous()
+        rb = rows[:B].contiguous()
+        y = torch.empty_like(xb)
+        sel = torch.empty(min(w.D, B * w.k_row), dtype=torch.int32, device=dev)
+        n_sel = torch.empty(1, dtype=torch.int32, device=dev)
+        work = torch.empty(max(sha.selective_mlp_workspace_bytes(B, w.d, w.D, sel.numel()), 1),
+                           dtype=torch.uint8, device=dev)
+        wsd = torch.empty(max(sha.selective_mlp_workspace_bytes(B, w.d, w.D, w.D), 1),
+                          dtype=torch.uint8, device=dev)
+        sha.mlp_union(rb, w.D, sel=sel, n_sel=n_sel, workspace=uws)
+        torch.cuda.synchronize()
+        n = int(n_sel.item())
+
+        def call(i):
+            sha.mlp_union(rb, w.D, sel=sel, n_sel=n_sel, stream=stream, workspace=uws)
+            a, b = ws[i % 2]
+            sha.selective_mlp(xb, a, b, sel, n_sel, n_max=sel.numel(), out=y, workspace=work,
+                              stream=stream)
+
+        def dcall(i):
+            a, b = ws[i % 2]
+            sha.selective_mlp(xb, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd, stream=stream)
+
+        ms, _ = time_calls(call, args.steps, args.warmup, stream)
+        dms, _ = time_calls(dcall, args.steps, args.warmup, stream)
+        pt = {"B": B, "union": n, "union_frac": round(n / w.D, 4),
+              "selective_us": round(ms * 1e3, 2), "all_neurons_us": round(dms * 1e3, 2),
+              "speedup": round(dms / ms, 3), "ideal": round(w.D / max(n, 1), 3),
+              "selective_GBps": round(n * w.weight_bytes_per_neuron / (ms / 1e3) / 1e9, 1)}
+        points.append(pt)
+        print(json.dumps(pt), flush=True)
+        B *= 2
+    out = {"metric": f"selective MLP speedup vs all neurons across batch unions, {w.name}",
+           "dtype": w.dtype, "data": "synthetic: seeded N(0,1) x, N(0,1/d) / N(0,1/D) weights, "
+                                     f"{w.k_row} uniform neurons per row",
+           "config": {"workload": w.name, "d": w.d, "D": w.D, "k_row": w.k_row},
+           "steps": args.steps, "warmup": args.warmup, "points": points}
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def bench_router(args):
     """Attention router of one layer on one GPU: scores = x W^T + b over the
     token's hidden state (d_model = H * d) and the per-row top-k written as the
@@ -644,6 +707,9 @@ def main():
         sys.exit(2)
     if args.decode_step:
         bench_step(args)
+        return
+    if args.mlp and args.mlp_sweep:
+        bench_mlp_sweep(args)
         return
     if args.mlp:
         bench_mlp(args)
