@@ -639,8 +639,10 @@ sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_
   if (!workspace || workspace_bytes < sha_mlp_union_workspace_bytes(D)) return SHA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
   (void)hipGetLastError();
+  // SHA_MLP_UNION_SMALL=0 (a tuning hook) keeps small unions on the three-kernel path.
   const hipError_t e = sha::launch_mlp_union(row_neurons, static_cast<int>(total), D, sel, n_sel,
-                                             static_cast<uint8_t*>(workspace), stream);
+                                             static_cast<uint8_t*>(workspace),
+                                             env_int("SHA_MLP_UNION_SMALL", 1) != 0, stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;
     return SHA_ERR_HIP;

@@ -179,6 +179,65 @@ __global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_write_kernel
   if (blockIdx.x == gridDim.x - 1 && tid == 0) *n_sel = static_cast<int32_t>(base + n_block);
 }
 
+// Small unions in one launch: one 1024-thread workgroup keeps a bit per
+// neuron in LDS (cleared, then set by every row entry with LDS atomic ors,
+// eight entries per thread in flight), then each thread counts the bits of
+// its run of words, a workgroup scan gives its output offset, and it writes
+// its neurons in ascending order; the last thread writes the total.  Used
+// for at most kSmallUnionMaxTotal entries and kSmallUnionMaxD neurons (one
+// workgroup reads every entry); it needs no workspace and gives the same
+// sel and count as the three kernels above.
+constexpr int kSmallUnionThreads = 1024;
+constexpr int kSmallUnionMaxD = 1 << 18;       // 32 KiB of LDS bits
+constexpr int kSmallUnionMaxTotal = 1 << 13;   // past ~8K entries the three kernels win
+
+__global__ __launch_bounds__(kSmallUnionThreads) void sha_mlp_union_small_kernel(
+    const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel) {
+  __shared__ uint32_t bits[kSmallUnionMaxD / 32];
+  __shared__ uint32_t wave_sums[kSmallUnionThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (D + 31) / 32;
+  for (int w = tid; w < nw; w += kSmallUnionThreads) bits[w] = 0u;
+  __syncthreads();
+  for (int i0 = 0; i0 < total; i0 += 8 * kSmallUnionThreads) {
+    int j[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kSmallUnionThreads + tid;
+      j[u] = i < total ? rows[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j[u] >= 0 && j[u] < D) atomicOr(&bits[j[u] >> 5], 1u << (j[u] & 31));
+  }
+  __syncthreads();
+  // Thread t owns words [t per, (t + 1) per) (ascending neurons in thread order).
+  const int per = (nw + kSmallUnionThreads - 1) / kSmallUnionThreads;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int q = 0; q < wave; ++q) before += wave_sums[q];
+  incl += before;
+  uint32_t pos = incl - cnt;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      sel[pos++] = w * 32 + (__ffs(m) - 1);
+      m &= m - 1u;
+    }
+  }
+  if (tid == kSmallUnionThreads - 1) *n_sel = static_cast<int32_t>(incl);
+}
+
 // ---------------------------------------------------------------------------
 // up projection: H = relu(x W1t[S]^T)
 // ---------------------------------------------------------------------------
@@ -668,7 +727,12 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
 int mlp_union_blocks(int D) { return (D + kUnionBlockFlags - 1) / kUnionBlockFlags; }
 
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, hipStream_t st) {
+                            uint8_t* flags, bool allow_small, hipStream_t st) {
+  if (allow_small && total <= kSmallUnionMaxTotal && D <= kSmallUnionMaxD) {
+    hipLaunchKernelGGL(sha_mlp_union_small_kernel, dim3(1), dim3(kSmallUnionThreads), 0, st, rows,
+                       total, D, sel, n_sel);
+    return hipGetLastError();
+  }
   const int n16 = (D + 15) / 16;
   hipLaunchKernelGGL(sha_mlp_union_clear_kernel, dim3(min((n16 + 255) / 256, 1024)), dim3(256), 0,
                      st, flags, D);

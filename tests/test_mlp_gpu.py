@@ -37,9 +37,17 @@ def _run(x, w1t, w2t, sel, n_sel, n_max=None):
 @pytest.mark.parametrize("B,k,D", [(1, 5, 100), (7, 40, 1000), (64, 300, 5000), (3, 0, 10),
                                    (5, 33, 40000), (9, 500, 100000), (64, 3686, 36864),
                                    (2, 70000, 65537), (16, 1638, 16384), (16, 4096, 65536),
-                                   (16, 4097, 65536), (1, 1, 1), (3, 7, 65536), (8, 3686, 36864)])
-def test_union_matches_oracle(B, k, D):
-    say(f"[mlp] union B={B} k={k} D={D}")
+                                   (16, 4097, 65536), (1, 1, 1), (3, 7, 65536), (8, 3686, 36864),
+                                   (2, 4096, 262144), (1, 8193, 262144), (2, 100, 262145),
+                                   (1, 8192, 300000), (4, 2048, 1000)])
+@pytest.mark.parametrize("path", ["auto", "three_kernels"])
+def test_union_matches_oracle(B, k, D, path, monkeypatch):
+    """Unions of at most 8192 entries and 2^18 neurons run in one workgroup
+    unless SHA_MLP_UNION_SMALL=0; larger ones (entries or neurons) always take
+    the three-kernel path."""
+    if path == "three_kernels":
+        monkeypatch.setenv("SHA_MLP_UNION_SMALL", "0")
+    say(f"[mlp] union B={B} k={k} D={D} {path}")
     rng = np.random.default_rng(B * 1000 + k)
     rows = rng.integers(-2, D + 3, size=(B, k)).astype(np.int32)
     sel, n_sel = sha.mlp_union(torch.from_numpy(rows).to(DEV), D)
