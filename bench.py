@@ -6,12 +6,20 @@ A step is one SHA decode layer call (split kernel + combine when split) over
 one batch of synthetic decode state already resident in HBM.  Prints one
 JSON line: effective KV bandwidth on active-head K/V bytes (the value), the
 per-call time, the roofline of the decode kernel (HIP-event durations on the
-launch stream), the same kernel with every head active, and the fp64 oracle
-timed on the host cores.
+launch stream), the same kernel with every head active, the fp64 oracle
+timed on the host cores, and (default workload) a density sweep over the
+active heads and a per-workload block for the other layer shapes.
 
-Other modes (profiling helpers, no JSON line):
-  --copy-calib   plain device-to-device copies of a known size, for scaling
-                 rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes.
+Other modes (one JSON line each):
+  --kv-layout L        the decode call on a strided or paged KV cache.
+  --mlp NAME           the selective MLP (device union + up/down projections);
+    --mlp-batch B      another batch size;  --mlp-sweep  batches 1, 2, 4, ...
+  --router NAME        the attention router (device time per call in a graph).
+  --decode-step L      an L-layer decode step (router, SHA, selective MLP).
+Profiling helpers:
+  --copy-calib         plain device-to-device copies of a known size, for
+                       scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes.
+  --summarize-traffic  counter CSVs -> profiles/traffic_<workload>.json.
 """
 from __future__ import annotations
 
