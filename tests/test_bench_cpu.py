@@ -11,9 +11,9 @@ BENCH = os.path.join(ROOT, "bench.py")
 
 
 def test_more_than_one_gpu_is_refused():
-    # Every mode (decode, MLP, router, decode step) measures one GPU.
-    for extra in ([], ["--mlp", "opt66b_mlp_bf16"], ["--router", "opt66b_f16"],
-                  ["--decode-step", "2"]):
+    # Every mode (decode, MLP, MLP sweep, router, decode step) measures one GPU.
+    for extra in ([], ["--mlp", "opt66b_mlp_bf16"], ["--mlp", "opt66b_mlp_bf16", "--mlp-sweep"],
+                  ["--router", "opt66b_f16"], ["--decode-step", "2"]):
         r = subprocess.run([sys.executable, BENCH, "--gpus", "2"] + extra, capture_output=True,
                            text=True, timeout=300)
         assert r.returncode == 2, extra
