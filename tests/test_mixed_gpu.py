@@ -122,11 +122,27 @@ def _mlp_case(i):
     return wl.MlpWorkload(f"mixed_mlp{i}", B=B, d=d, D=D, k_row=k_row, dtype=dtype, seed=60 + i), pad
 
 
+def _mlp_splits(i):
+    """Forced split counts for some cases (0: the planner's), from their own
+    seed so the shapes above do not depend on them."""
+    rng = np.random.default_rng(9600 + i)
+    return int(rng.choice([0, 0, 1, 2, 3, 8])), int(rng.choice([0, 0, 1, 2, 5]))
+
+
 @pytest.mark.parametrize("i", range(N_MLP))
-def test_mixed_selective_mlp(i):
+def test_mixed_selective_mlp(i, monkeypatch):
+    """Batches of 1-140 rows (every batch-block form, 1-3 batch tiles), with
+    the planner's split counts or forced ones (SHA_MLP_UP_SPLITS /
+    SHA_MLP_DN_SPLITS, read by the library on every call)."""
     from oracle import mlp_union_ref, selective_mlp_ref
     w, pad = _mlp_case(i)
-    say(f"[mixed mlp {i}] {w.dtype} B={w.B} d={w.d} D={w.D} k_row={w.k_row} pad={pad}")
+    us, ds = _mlp_splits(i)
+    if us:
+        monkeypatch.setenv("SHA_MLP_UP_SPLITS", str(us))
+    if ds:
+        monkeypatch.setenv("SHA_MLP_DN_SPLITS", str(ds))
+    say(f"[mixed mlp {i}] {w.dtype} B={w.B} d={w.d} D={w.D} k_row={w.k_row} pad={pad} "
+        f"up_splits={us or 'plan'} dn_splits={ds or 'plan'}")
     x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
     if pad and w.k_row > 0:                            # entries outside [0, D) are skipped
         rows = rows.clone()
