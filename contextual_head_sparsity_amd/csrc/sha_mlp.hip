@@ -14,6 +14,8 @@
 //            then every 4096-flag block counts the flags before it (its
 //            output offset), writes its marked neurons in ascending order,
 //            and the last block writes the total (deterministic, on device).
+//            Up to 8192 row entries, one workgroup does all of it with the
+//            flags as LDS bits (one launch).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
 //            a workgroup owns 128 selected neurons x 64 batch rows over a K
 //            range; weight rows stream in 256-byte runs (non-temporal
@@ -27,6 +29,9 @@
 //            (ds_read_b64_tr_b16) as B operands, H comes from LDS as A.
 //            Split ranges of neurons write fp32 partials that
 //            `down_finalize` sums in a fixed order.
+//   Batches of at most 16 (32) rows compute only the 1 (2) batch blocks of
+//   16 rows that hold rows: in the up projection the waves then split the
+//   tile's neurons instead of its batch blocks.
 // The selection count is read on the device, so union -> up -> down needs no
 // host synchronisation; grids are sized for the caller's upper bound n_max
 // and workgroups past the actual count exit or mask.
