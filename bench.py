@@ -14,7 +14,8 @@ Other modes (one JSON line each):
   --kv-layout L        the decode call on a strided or paged KV cache.
   --mlp NAME           the selective MLP (device union + up/down projections);
     --mlp-batch B      another batch size;  --mlp-sweep  batches 1, 2, 4, ...
-  --router NAME        the attention router (device time per call in a graph).
+  --router NAME        the attention router (device time per call in a graph;
+                       --router-floor adds the same graph on tiny inputs).
   --decode-step L      an L-layer decode step (router, SHA, selective MLP).
 Profiling helpers:
   --copy-calib         plain device-to-device copies of a known size, for
@@ -110,6 +111,8 @@ def parse():
                    help="MLP shape inside the decode step (its dtype follows the workload)")
     p.add_argument("--router", default=None, choices=list(wl.WORKLOADS),
                    help="time the attention router (scores + per-row top-k) of this layer shape")
+    p.add_argument("--router-floor", action="store_true",
+                   help="with --router: also time the same graph of calls on tiny inputs")
     return p.parse_args()
 
 
@@ -545,7 +548,9 @@ def bench_router(args):
     so every call reads its weights from HBM), replayed and divided by the
     number of calls.  Also reported: the same with one weight matrix (warm
     caches), and call by call from Python (binding and launch overhead
-    included; HIP events around each call)."""
+    included; HIP events around each call), and with --router-floor the
+    launch floor: the same graph of calls on tiny inputs (one launch, two
+    launches, and this layer's grids with a 64-wide hidden state)."""
     w = wl.WORKLOADS[args.router]
     dev = torch.device("cuda:0")
     dt = wl.DTYPES[w.dtype]
@@ -602,6 +607,25 @@ def bench_router(args):
 
     g_cold = graph_us(captured(lambda i: ws[i % copies]), copies)
     g_warm = graph_us(captured(lambda i: w0), copies)
+
+    def tiny(B, dm_, nh_, k):
+        # the launch floor: the same graph of calls on a 64-wide hidden state
+        xt = torch.randn(B, dm_, generator=g, device=dev).to(dt)
+        wt = torch.randn(nh_, dm_, generator=g, device=dev).to(dt)
+        it = torch.empty(B, k, dtype=torch.int32, device=dev) if k else None
+        st = torch.empty(B, nh_, dtype=torch.float32, device=dev)
+
+        def call(i):
+            sha.router_topk(xt, wt, k, index=it, scores=st, stream=torch.cuda.current_stream(dev))
+        return round(graph_us(call, 2000), 2)
+
+    floor = None
+    if getattr(args, "router_floor", False):
+        floor = {"scores_only_B1_d64_H8": tiny(1, 64, 8, 0),
+                 "scores_topk_B1_d64_H8_k3": tiny(1, 64, 8, 3),
+                 f"same_grid_d64_B{w.B}_H{nh}_k{w.top_k}": tiny(w.B, 64, nh, w.top_k),
+                 "note": "graph device time per call of the same entry point on tiny inputs: "
+                         "one launch, two launches, and this layer's grids with a 64-wide row"}
     ms, ev = time_calls(cold, args.steps, args.warmup, stream)
     wms, wev = time_calls(warm, args.steps, args.warmup, stream)
     nbytes = wbytes + w.B * dm * e + w.B * nh * 4 + w.B * w.top_k * 4
@@ -619,6 +643,7 @@ def bench_router(args):
                         "note": "device time per call in a graph; at 8 TB/s the bytes alone "
                                 f"would take {nbytes / HBM_PEAK_GBS / 1e3:.2f} us"},
            "warm_weights": {"graph_us_per_call": round(g_warm, 2)},
+           **({"launch_floor": floor} if floor else {}),
            "call_by_call": {"cold_us_per_call": round(ms * 1e3, 2),
                             "cold_event_us": round(float(np.mean(ev)) * 1e3, 2),
                             "warm_us_per_call": round(wms * 1e3, 2),

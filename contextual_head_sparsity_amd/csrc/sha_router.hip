@@ -15,11 +15,13 @@
 //                  pieces (v_dot2 for 16-bit inputs, fp32 accumulation), DPP
 //                  + shuffle wave sums, the waves' partials added in a fixed
 //                  order.
-//   top-k kernel : one wave per batch row; each head's rank in the (score
-//                  descending, index ascending) order is counted against the
-//                  row staged in LDS (NaN ranked as -inf) and the heads of
-//                  rank < k are written in ascending order with a ballot
-//                  prefix count.
+//   top-k kernel : one workgroup of four waves per batch row; each head's
+//                  rank in the (score descending, index ascending) order
+//                  (NaN ranked as -inf) is a count of larger 64-bit keys
+//                  (order-preserving score bits, then the inverted head id)
+//                  staged in LDS, each wave counting a quarter of the row;
+//                  the heads of rank < k are written in ascending order with
+//                  a ballot prefix count.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +41,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 constexpr int kScoreWaves = 8;  // waves per scores workgroup
+constexpr int kTopkWaves = 4;   // waves per top-k workgroup (one batch row)
 
 // One workgroup per (batch row, HEADS consecutive heads).  The hidden
 // dimension is cut into blocks of 64 16-byte pieces and wave w takes blocks
@@ -104,69 +107,79 @@ __global__ __launch_bounds__(kScoreWaves * 64) void sha_router_scores_kernel(Rou
   }
 }
 
-// (value, index) ordering of the top-k: larger value first, then lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Sort key of head h with score x in the (score descending, index
+// ascending) order: a larger key ranks first.  NaN becomes -inf and -0
+// becomes +0 (equal floats, equal keys); the float's bits are mapped to an
+// unsigned integer of the same order (sign bit set: all bits flipped, else
+// the sign bit flipped), and the low word holds ~h so that of two equal
+// scores the lower head id has the larger key.
+__device__ __forceinline__ unsigned long long topk_key(float x, int h) {
+  x = (x != x) ? kNegInf : (x == 0.f ? 0.f : x);
+  unsigned u = __float_as_uint(x);
+  u ^= (u >> 31) ? 0xffffffffu : 0x80000000u;
+  return (static_cast<unsigned long long>(u) << 32) | static_cast<unsigned>(~h);
 }
 
-// One wave per batch row.  Head h is picked when fewer than top_k heads rank
-// before it in the (score descending, index ascending) order, NaN ranked as
-// -inf: every lane counts, for its heads, how many of the row's H scores
-// (staged in LDS, read as broadcasts) come first.  The picked heads are then
-// written in ascending order with a ballot prefix count.  SLOTS = heads per
-// lane (H <= 64 SLOTS), a compile-time count so that the counting loop has
-// no branches.
+// One workgroup of 4 waves per batch row.  Head h is picked when fewer than
+// top_k heads rank before it, i.e. have a larger key.  The row's keys are
+// staged in LDS (64 SLOTS entries; those past H hold -inf with an index of
+// H or more, so they never rank before a real head); wave w counts, for
+// every head, the larger keys among entries [w Q, (w + 1) Q), read as
+// broadcasts, and wave 0 adds the four counts and writes the picked heads
+// in ascending order with a ballot prefix count.  SLOTS = heads per lane
+// (H <= 64 SLOTS), a compile-time count so that the loops have no
+// branches.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void sha_router_topk_kernel(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) float row_sc[4][64 * SLOTS];
+__global__ __launch_bounds__(kTopkWaves * 64) void sha_router_topk_kernel(RouterArgs a) {
+  constexpr int N = 64 * SLOTS;
+  constexpr int Q = N / kTopkWaves;
+  __shared__ unsigned long long keys[N];
+  __shared__ int part[kTopkWaves][N];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x * 4 + wave;
-  if (b >= a.B) return;
+  const int b = blockIdx.x;
   const float* srow = a.scores + static_cast<size_t>(b) * a.H;
-  float* sc = row_sc[wave];
-  float v[SLOTS];
-  // Unconditional (clamped) loads, all in flight together.
 #pragma unroll
-  for (int i = 0; i < SLOTS; ++i) v[i] = srow[min(lane + 64 * i, a.H - 1)];
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int h = lane + 64 * i;
-    float x = v[i];
-    x = (h >= a.H || x != x) ? kNegInf : x;  // NaN ranks like -inf
-    v[i] = x;
-    // Entries past H hold -inf: with an index of H or more they never rank
-    // before a real head.
-    sc[h] = x;
+  for (int i = 0; i < (N + kTopkWaves * 64 - 1) / (kTopkWaves * 64); ++i) {
+    const int h = threadIdx.x + kTopkWaves * 64 * i;
+    if (h < N) keys[h] = topk_key(h < a.H ? srow[h] : kNegInf, h);
   }
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();
+  unsigned long long mine[SLOTS];
   int rank[SLOTS];
 #pragma unroll
-  for (int i = 0; i < SLOTS; ++i) rank[i] = 0;
-  for (int h2 = 0; h2 < a.H; h2 += 4) {
-    const float4 o4 = *reinterpret_cast<const float4*>(sc + h2);
-    const float o[4] = {o4.x, o4.y, o4.z, o4.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int i = 0; i < SLOTS; ++i)
-        rank[i] += better(o[e], h2 + e, v[i], lane + 64 * i) ? 1 : 0;
+  for (int i = 0; i < SLOTS; ++i) {
+    mine[i] = keys[lane + 64 * i];
+    rank[i] = 0;
   }
+#pragma unroll
+  for (int o = 0; o < Q; ++o) {
+    const unsigned long long k = keys[wave * Q + o];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) rank[i] += k > mine[i] ? 1 : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) part[wave][lane + 64 * i] = rank[i];
+  __syncthreads();
+  if (wave != 0) return;
   int base = 0;
   int32_t* irow = a.index + static_cast<size_t>(b) * a.top_k;
 #pragma unroll
   for (int i = 0; i < SLOTS; ++i) {
     const int h = lane + 64 * i;
-    const bool mine = h < a.H && rank[i] < a.top_k;
-    const unsigned long long mask = __ballot(mine);
-    if (mine) irow[base + __popcll(mask & ((1ull << lane) - 1ull))] = h;
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) r += part[w][h];
+    const bool mine_pick = h < a.H && r < a.top_k;
+    const unsigned long long mask = __ballot(mine_pick);
+    if (mine_pick) irow[base + __popcll(mask & ((1ull << lane) - 1ull))] = h;
     base += __popcll(mask);
   }
 }
 
 template <int SLOTS>
 hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((sha_router_topk_kernel<SLOTS>), dim3(static_cast<unsigned>((a.B + 3) / 4)),
-                     dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sha_router_topk_kernel<SLOTS>), dim3(static_cast<unsigned>(a.B)),
+                     dim3(kTopkWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
