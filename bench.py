@@ -152,6 +152,32 @@ def time_calls(call, steps: int, warmup: int, stream):
     return wall / steps * 1e3, ev_ms
 
 
+def graph_us_per_call(call, n: int, dev, warm: int, reps: int) -> float:
+    """Device time per call as a captured decode loop sees it: `call(i)` for
+    i < n captured in one graph on a side stream (calls launch on the current,
+    i.e. capturing, stream), replayed `warm` times untimed and `reps` times
+    timed; wall time of the replays over reps * n."""
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        for i in range(3):
+            call(i)
+    s.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for i in range(n):
+            call(i)
+    torch.cuda.synchronize()
+    for _ in range(warm):
+        gr.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gr.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / (reps * n) * 1e6
+
+
 def read_probe(dev, nbytes: int = 1 << 31):
     """Secondary ceiling: the best streaming-read rate of libsha_probe.so (the
     head kernel's access pattern: 1 KiB non-temporal wave loads, 8 in flight)
@@ -481,7 +507,9 @@ def bench_mlp_sweep(args):
     (x = the first B rows, each row's neurons the workload's seeded draw, so
     a smaller batch's rows are a prefix of a larger one's).  Per point: union
     size, µs per selective call (device union + MLP), µs per all-neurons call,
-    speedup and its ideal D / |union|."""
+    speedup and its ideal D / |union|; wall time over back-to-back calls from
+    Python, and device time per call with the same calls captured in a HIP
+    graph (no host launch overhead)."""
     w = wl.MLP_WORKLOADS[args.mlp]
     dev = torch.device("cuda:0")
     x, w1t, w2t, rows = wl.make_mlp(w, dev)
@@ -506,22 +534,30 @@ def bench_mlp_sweep(args):
         torch.cuda.synchronize()
         n = int(n_sel.item())
 
-        def call(i):
-            sha.mlp_union(rb, w.D, sel=sel, n_sel=n_sel, stream=stream, workspace=uws)
+        def call(i, st=None):
+            st = st or stream
+            sha.mlp_union(rb, w.D, sel=sel, n_sel=n_sel, stream=st, workspace=uws)
             a, b = ws[i % 2]
             sha.selective_mlp(xb, a, b, sel, n_sel, n_max=sel.numel(), out=y, workspace=work,
-                              stream=stream)
+                              stream=st)
 
-        def dcall(i):
+        def dcall(i, st=None):
             a, b = ws[i % 2]
-            sha.selective_mlp(xb, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd, stream=stream)
+            sha.selective_mlp(xb, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd,
+                              stream=st or stream)
 
         ms, _ = time_calls(call, args.steps, args.warmup, stream)
         dms, _ = time_calls(dcall, args.steps, args.warmup, stream)
+        # the same calls captured in a graph (launch overhead removed)
+        ng = 20
+        gs = graph_us_per_call(lambda i: call(i, torch.cuda.current_stream(dev)), ng, dev, 2, 5)
+        gd = graph_us_per_call(lambda i: dcall(i, torch.cuda.current_stream(dev)), ng, dev, 2, 5)
         pt = {"B": B, "union": n, "union_frac": round(n / w.D, 4),
               "selective_us": round(ms * 1e3, 2), "all_neurons_us": round(dms * 1e3, 2),
               "speedup": round(dms / ms, 3), "ideal": round(w.D / max(n, 1), 3),
-              "selective_GBps": round(n * w.weight_bytes_per_neuron / (ms / 1e3) / 1e9, 1)}
+              "selective_GBps": round(n * w.weight_bytes_per_neuron / (ms / 1e3) / 1e9, 1),
+              "graph_selective_us": round(gs, 2), "graph_all_neurons_us": round(gd, 2),
+              "graph_speedup": round(gd / gs, 3)}
         points.append(pt)
         print(json.dumps(pt), flush=True)
         B *= 2
@@ -576,27 +612,7 @@ def bench_router(args):
         sha.router_topk(x, w0, w.top_k, bias=bias, index=idx, scores=sc, stream=stream)
 
     def graph_us(call, n):
-        """Device time per call: a graph of n calls, replayed."""
-        s = torch.cuda.Stream(device=dev)
-        s.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(s):
-            for i in range(3):
-                call(i)
-        s.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=s):
-            for i in range(n):
-                call(i)
-        torch.cuda.synchronize()
-        for _ in range(max(args.warmup // 50, 2)):
-            gr.replay()
-        torch.cuda.synchronize()
-        reps = max(args.steps // 50, 3)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            gr.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / (reps * n) * 1e6
+        return graph_us_per_call(call, n, dev, max(args.warmup // 50, 2), max(args.steps // 50, 3))
 
     def captured(weights_of):
         # calls on the current (capturing) stream
