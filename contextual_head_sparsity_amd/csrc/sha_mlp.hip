@@ -157,10 +157,21 @@ __global__ __launch_bounds__(kUnionBlockThreads) void sha_mlp_union_write_kernel
   __shared__ uint32_t base_sh;
   const int tid = threadIdx.x;
   const uint4* fw = reinterpret_cast<const uint4*>(flags);
-  // Output offset of this block: the set flags of the blocks before it.
+  // Output offset of this block: the set flags of the blocks before it,
+  // read eight words per thread at a time (unconditional loads, clamped to
+  // the last word before the block, all eight in flight, then counted where
+  // in range), so a late block waits for memory once per eight blocks
+  // before it rather than once per block.
   uint32_t part = 0;
   const int words_before = static_cast<int>(blockIdx.x) * kUnionBlockThreads;
-  for (int q = tid; q < words_before; q += kUnionBlockThreads) part += flag_count(fw[q]);
+  for (int q0 = tid; q0 < words_before; q0 += 8 * kUnionBlockThreads) {
+    uint4 f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f[u] = fw[min(q0 + u * kUnionBlockThreads, words_before - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      part += q0 + u * kUnionBlockThreads < words_before ? flag_count(f[u]) : 0u;
+  }
   uint32_t base;
   block_scan(part, wave_sums, &base);
   if (tid == 0) base_sh = base;
