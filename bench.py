@@ -8,7 +8,9 @@ JSON line: effective KV bandwidth on active-head K/V bytes (the value), the
 per-call time, the roofline of the decode kernel (HIP-event durations on the
 launch stream), the same kernel with every head active, the fp64 oracle
 timed on the host cores, and (default workload) a density sweep over the
-active heads and a per-workload block for the other layer shapes.
+active heads, a per-workload block for the other layer shapes, and short
+summaries of the selective MLP (OPT shapes) and the attention router (layer
+shapes) (--no-extras skips those two).
 
 Other modes (one JSON line each):
   --kv-layout L        the decode call on a strided or paged KV cache.
@@ -84,6 +86,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the selective-MLP and router summaries on the default line")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the per-workload block and the density sweep (headline only)")
     p.add_argument("--sweep-out", default=None,
@@ -498,7 +502,7 @@ def bench_mlp(args):
                            "GBps": round(w.D * w.weight_bytes_per_neuron / (dms / 1e3) / 1e9, 2),
                            "speedup_selective_vs_all": round(dms / ms, 3),
                            "ideal_speedup": round(w.D / max(n, 1), 3)}}
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def bench_mlp_sweep(args):
@@ -664,7 +668,7 @@ def bench_router(args):
                             "cold_event_us": round(float(np.mean(ev)) * 1e3, 2),
                             "warm_us_per_call": round(wms * 1e3, 2),
                             "note": "Python binding + launch per call, HIP events around each call"}}
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def to_pages(w, ks, vs, page, dev):
@@ -761,10 +765,10 @@ def main():
         bench_mlp_sweep(args)
         return
     if args.mlp:
-        bench_mlp(args)
+        print(json.dumps(bench_mlp(args)), flush=True)
         return
     if args.router:
-        bench_router(args)
+        print(json.dumps(bench_router(args)), flush=True)
         return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -910,7 +914,43 @@ def main():
             if name != w.name:
                 entries[name] = config_entry(wc, dev, csteps, cwarm, stream)
         out["configs"] = {n: entries[n] for n in wl.WORKLOADS}
+        if not args.no_extras:
+            out["selective_mlp"], out["router"] = extras(args)
     print(json.dumps(out), flush=True)
+
+
+def extras(args):
+    """The other two kernel families of the sparse layer, summarised for the
+    default line: the selective MLP at the two OPT MLP shapes (device union +
+    up/down projections, µs and effective weight GB/s, speedup against all
+    neurons) and the attention router at the four layer shapes (device time
+    per call in a HIP graph, weights read from HBM).  The full records come
+    from `--mlp NAME` and `--router NAME`."""
+    mlp = {}
+    for name in wl.MLP_WORKLOADS:
+        if name.startswith("tiny"):
+            continue
+        r = bench_mlp(argparse.Namespace(mlp=name, mlp_batch=0, steps=args.steps,
+                                         warmup=max(args.warmup, 10)))
+        a = r["all_neurons"]
+        mlp[name] = {"B": r["config"]["B"], "union_frac": r["config"]["union_frac"],
+                     "us_per_layer": r["us_per_layer"], "weight_GBps": r["value"],
+                     "pct_hbm_peak": r["pct_hbm_peak"], "all_neurons_us": a["us_per_layer"],
+                     "speedup_vs_all_neurons": a["speedup_selective_vs_all"],
+                     "ideal_speedup": a["ideal_speedup"]}
+        torch.cuda.empty_cache()
+    router = {}
+    for name, w in wl.WORKLOADS.items():
+        if name.startswith("tiny"):
+            continue
+        r = bench_router(argparse.Namespace(router=name, router_floor=False, steps=args.steps,
+                                            warmup=max(args.warmup, 20)))
+        router[name] = {"B": w.B, "heads": r["config"]["heads"], "top_k": w.top_k,
+                        "graph_us_per_call": r["value"],
+                        "graph_us_per_call_warm": r["warm_weights"]["graph_us_per_call"],
+                        "python_us_per_call": r["call_by_call"]["cold_us_per_call"]}
+        torch.cuda.empty_cache()
+    return mlp, router
 
 
 if __name__ == "__main__":
