@@ -19,7 +19,7 @@
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
 //            a workgroup owns 128 selected neurons x 64 batch rows over a K
 //            range; weight rows stream in 256-byte runs (non-temporal
-//            128-bit loads, two stages ahead) through swizzled LDS into A
+//            128-bit loads, three stages ahead) through swizzled LDS into A
 //            operands, x pieces come from L2 as B operands.  With one K
 //            split it applies ReLU and writes H (16-bit); with several it
 //            writes fp32 partials and `up_finalize` sums them.
