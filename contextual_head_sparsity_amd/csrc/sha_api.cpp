@@ -411,7 +411,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
 // selective MLP planning
 // ---------------------------------------------------------------------------
 struct MlpPlan {
-  int n_pad, b_pad, bb, up_splits, up_kper, dn_splits;
+  int n_pad, b_pad, bb, up_splits, up_kper, dn_splits, dn_waves;
   size_t h_bytes, up_bytes, dn_bytes;
 };
 
@@ -422,9 +422,10 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 //   up  : one workgroup per kMlpUpNeurons selected neurons x 64 batch rows
 //         (2 resident per CU); its K (d) is split in whole kMlpUpKc stages,
 //         ceil(0.95 x resident slots / workgroups) ways (at most 8).
-//   down: one workgroup per 256 output columns x 64 rows; the neuron range is
-//         split for about two workgroups per CU (each range keeps >= 64
-//         neurons, at most 64 splits).
+//   down: one workgroup per 512 output columns (8 waves, one per CU; 256
+//         columns and 4 waves, two per CU, when d is not a multiple of 512)
+//         x 64 rows; the neuron range is split for about one round of
+//         workgroups (each range keeps >= 64 neurons, at most 64 splits).
 // The constants come from split sweeps of the OPT MLPs on MI355X.
 constexpr int kUpWgsPerCu = 2;
 constexpr int kDownWgsPerCu = 2;
@@ -455,8 +456,17 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   if (us > kstages) us = kstages;
   p.up_kper = (kstages + us - 1) / us * sha::kMlpUpKc;
   p.up_splits = (d + p.up_kper - 1) / p.up_kper;
-  const long long dn_items = static_cast<long long>(d / 256) * (p.b_pad / 64);
-  long long ds = static_cast<long long>(kDownWgsPerCu) * cus / dn_items;
+  // Down workgroups: 8 waves x 64 columns, one per CU, when d is a multiple
+  // of 512 (each column block, and its read of H from L2, covers 512
+  // columns: OPT-66B down projection 137.5 -> 123.0 us against the 4-wave
+  // form), else 4 waves x 64 columns, two per CU; SHA_MLP_DN_WAVES = 4 or 8
+  // forces one where d allows (a tuning hook).
+  const int dn_env = env_int("SHA_MLP_DN_WAVES", 0);
+  p.dn_waves = (d % 512 == 0 && dn_env != 4) ? 8 : 4;
+  const int dn_cols = 64 * p.dn_waves;
+  const int dn_per_cu = p.dn_waves == 8 ? kDownWgsPerCu / 2 : kDownWgsPerCu;
+  const long long dn_items = static_cast<long long>(d / dn_cols) * (p.b_pad / 64);
+  long long ds = static_cast<long long>(dn_per_cu) * cus / dn_items;
   const long long ds_max = n_max / 64 > 1 ? n_max / 64 : 1;
   if (ds > ds_max) ds = ds_max;
   if (ds > 64) ds = 64;
@@ -697,6 +707,7 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.up_splits = p.up_splits;
   a.up_kper = p.up_kper;
   a.dn_splits = p.dn_splits;
+  a.dn_waves = p.dn_waves;
   (void)hipGetLastError();
   const hipError_t e = sha::launch_selective_mlp(a, dtype, stream);
   if (e != hipSuccess) {

@@ -35,6 +35,8 @@ struct MlpArgs {
                         // computed, read for an output row, or stored
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
+  int dn_waves;         // waves per down workgroup (64 output columns each): 4, or 8
+                        // when d is a multiple of 512
 };
 
 // flags: round_up(D, 256) bytes of workspace.

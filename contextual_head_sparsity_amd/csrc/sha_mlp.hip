@@ -495,19 +495,24 @@ __global__ __launch_bounds__(256) void sha_mlp_up_finalize_kernel(MlpArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;                    // accelerator dies (XCDs) of MI355X
 constexpr int kDnKc = 64;                   // neurons per LDS chunk (2 MFMA K steps)
-constexpr int kDnCols = 256;                // output columns per workgroup
-constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 B: conflict-free transposed reads
 constexpr int kDnHPitch = kDnKc * 2 + 16;   // 144 B: conflict-free H reads
 
-// Two workgroups per CU (the planner's assumption): the register budget is
-// held at 256 per lane, accumulators included.  BB = 16-row batch blocks
-// computed per 64-row tile (as in the up projection): only those rows of H
-// are loaded and multiplied.
-template <int DT, int BB>
-__global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
+// NW = waves per workgroup: each wave owns 64 output columns, so a
+// workgroup owns 64 NW columns (256 with 4 waves, two workgroups per CU; 512
+// with 8 waves, one per CU, which halves the H rows every column block
+// reads).  The register budget is 256 per lane either way, accumulators
+// included.  BB = 16-row batch blocks computed per 64-row tile (as in the up
+// projection): only those rows of H are multiplied.
+template <int DT, int BB, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a) {
   using M = Mx<DT>;
   static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
-  constexpr int HL = BB == 4 ? 2 : 1;         // H pieces per thread (32 rows each)
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  constexpr int T = 64 * NW;                  // threads
+  constexpr int kDnCols = 64 * NW;            // output columns per workgroup
+  constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 / 1056 B: conflict-free transposed reads
+  constexpr int RP = kDnCols / 8;             // 16-byte pieces per weight row
+  constexpr int HL = (BB == 4 ? 512 : 256) / T > 0 ? (BB == 4 ? 512 : 256) / T : 1;  // H pieces per thread
   __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
   __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
   const int n_sel = sel_count(a);
@@ -541,13 +546,15 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Gathered W2t rows of a chunk: 64 rows x 512 B = 2048 pieces (8 per
-  // thread); H chunk: 32 HL rows x 128 B = 256 HL pieces (HL per thread; at
-  // least the 16 BB computed rows), neurons at or past nend read as zero.  Piece tid + 256 i of the weights is row
-  // 2 wave + (lane >> 5) + 8 i, so each load instruction needs two selection
-  // entries that are the same for the whole wave: they are read with scalar
-  // loads (own counter), and the vector loads of earlier chunks need not
-  // complete before the next chunk's addresses are known.  H pieces are read
+  // Gathered W2t rows of a chunk: 64 rows x 128 NW bytes = 512 NW pieces (8
+  // per thread); H chunk: HL T / 8 rows x 128 B (HL pieces per thread; at
+  // least the 16 BB computed rows), neurons at or past nend read as zero.
+  // Piece tid + T i of the weights is row tid / RP + 8 i: with 4 waves each
+  // load instruction covers two rows (2 wave + (lane >> 5)), with 8 waves
+  // one (wave), so it needs one or two selection entries that are the same
+  // for the whole wave: they are read with scalar loads (own counter), and
+  // the vector loads of earlier chunks need not complete before the next
+  // chunk's addresses are known.  H pieces are read
   // unconditionally (offsets clamped inside the row) and masked only when
   // they are written to LDS: masking at load time would make the wave wait
   // for them, and (loads complete in order) for every older load, at once.
@@ -556,16 +563,22 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
   auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[HL]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r0 = k0 + 2 * wu + 8 * i;
-      const int s0 = a.sel[min(r0, nend - 1)], s1 = a.sel[min(r0 + 1, nend - 1)];
-      const int row0 = (s0 >= 0 && s0 < a.D) ? s0 : 0, row1 = (s1 >= 0 && s1 < a.D) ? s1 : 0;
-      const int row = upper ? row1 : row0;
+      int row;
+      if constexpr (NW == 4) {
+        const int r0 = k0 + 2 * wu + 8 * i;
+        const int s0 = a.sel[min(r0, nend - 1)], s1 = a.sel[min(r0 + 1, nend - 1)];
+        const int row0 = (s0 >= 0 && s0 < a.D) ? s0 : 0, row1 = (s1 >= 0 && s1 < a.D) ? s1 : 0;
+        row = upper ? row1 : row0;
+      } else {
+        const int s0 = a.sel[min(k0 + wu + 8 * i, nend - 1)];
+        row = (s0 >= 0 && s0 < a.D) ? s0 : 0;
+      }
       wv[i] = ld16_stream(static_cast<const char*>(a.w2t) +
-                          (static_cast<size_t>(row) * a.d + col0 + (lane & 31) * 8) * 2);
+                          (static_cast<size_t>(row) * a.d + col0 + (lane % RP) * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < HL; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = tid + T * i;
       const int r = idx >> 3, piece = idx & 7;
       const int nc = min(k0 + piece * 8, a.n_pad - 8);  // past n_pad: past nend, masked
       hv[i] = ld16(static_cast<const char*>(a.h) +
@@ -583,13 +596,13 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_down_kernel(MlpArgs a) {
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 5, piece = idx & 31;
+      const int idx = tid + T * i;
+      const int r = idx / RP, piece = idx % RP;
       *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, w[i]);
     }
 #pragma unroll
     for (int i = 0; i < HL; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = tid + T * i;
       const int r = idx >> 3, piece = idx & 7;
       const int cnt = min(max(nend - (nbeg + j * kDnKc + piece * 8), 0), 8);  // valid neurons
       uint32_t m[4];
@@ -701,6 +714,7 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
 
 template <int DT, int BB>
 hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
+  const int dn_cols = 64 * a.dn_waves;
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
   const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
   hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
@@ -715,9 +729,11 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   }
   // 1-D over (column block, split, batch tile): the kernel maps the ids
   // onto XCDs itself.
-  hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB>),
-                     dim3(static_cast<unsigned>((a.d / kDnCols) * a.dn_splits) * btiles),
-                     dim3(256), 0, st, a);
+  const dim3 dn_grid(static_cast<unsigned>((a.d / dn_cols) * a.dn_splits) * btiles);
+  if (a.dn_waves == 8)
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 8>), dn_grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 4>), dn_grid, dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dn_splits > 1) {
     const size_t total = static_cast<size_t>(a.B) * (a.d / 4);

@@ -58,6 +58,36 @@ def test_union_matches_oracle(B, k, D, path, monkeypatch):
     assert np.array_equal(sel[:n].cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("B,d,D,k_row", [(1, 4096, 16384, 1638), (16, 1024, 3000, 200),
+                                         (40, 512, 2000, 150), (70, 512, 900, 60),
+                                         (5, 768, 1000, 100)])
+def test_down_waves_agree(B, d, D, k_row, monkeypatch):
+    """The 4-wave (256-column) and 8-wave (512-column) down workgroups give
+    bit-identical outputs at the same split count (each output sums the
+    same neuron chunks in the same order) and both match the oracle; a width
+    that is not a multiple of 512 keeps the 4-wave form."""
+    say(f"[mlp] down waves B={B} d={d} D={D} k_row={k_row}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 5 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    outs = {}
+    for splits in ("3", None):
+        for waves in ("4", "8"):
+            monkeypatch.setenv("SHA_MLP_DN_WAVES", waves)
+            if splits:
+                monkeypatch.setenv("SHA_MLP_DN_SPLITS", splits)
+            else:
+                monkeypatch.delenv("SHA_MLP_DN_SPLITS", raising=False)
+            y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+            torch.cuda.synchronize()
+            err = float(np.abs(y.cpu().double().numpy() - ref).max())
+            assert err <= _tol("bf16", ref), (waves, splits, err)
+            outs[(splits, waves)] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs[("3", "4")]), wl.raw_bits(outs[("3", "8")]))
+
+
 def test_union_rows_not_16_byte_aligned():
     """Row lists need only 4-byte alignment (here 4 bytes past a 16-byte
     boundary)."""
