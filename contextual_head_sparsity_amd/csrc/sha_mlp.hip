@@ -458,6 +458,171 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   }
 }
 
+// One computed batch block (B <= 16): the four waves of the 128-neuron
+// workgroup all multiply the same 16 x rows, so instead of each loading all
+// of them, wave w loads piece column w of each row (one 16-byte piece per
+// lane per stage) two stages ahead, writes the pieces of stage st + 1 into
+// a double-buffered 16-row x tile in LDS (XOR-swizzled like the weights,
+// 2 x 4 KB), and every wave reads its B operands there: each x byte is read
+// from L2 once per workgroup instead of four times.  Weights move exactly
+// as in the general form; per neuron the products accumulate over the same
+// K stages in the same order, so its outputs are bit-identical.
+constexpr int kUp1N = kMlpUpNeurons;        // neurons per workgroup (128)
+constexpr int kUp1Loads = kUp1N * kUpPieces / 256;  // weight pieces per thread per stage
+
+struct UpW1 {
+  uint4 v[kUp1Loads];
+};
+struct UpX1 {
+  uint4 v[1];
+};
+
+template <int DT>
+__global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
+  using M = Mx<DT>;
+  constexpr int NBW = 2;                      // neuron blocks per wave
+  __shared__ __attribute__((aligned(16))) char wsm_[2 * kUp1N * kUpRowB];
+  __shared__ __attribute__((aligned(16))) char xsm_[2 * 16 * kUpRowB];
+  const int nblocks = a.n_pad / kUp1N;
+  int t = blockIdx.x;
+  const int nblk = t % nblocks;
+  t /= nblocks;
+  const int split = t % a.up_splits;
+  const int btile = t / a.up_splits;
+  const int n_sel = sel_count(a);
+  const int n0 = nblk * kUp1N;
+  if (n0 >= n_sel) return;                    // whole workgroup: past the selection
+  const int b0 = btile * 64;
+  const int kbeg = split * a.up_kper;
+  const int kend = min(kbeg + a.up_kper, a.d);
+  const int nst = kend > kbeg ? (kend - kbeg) / kUpKc : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, c = lane & 15;
+  lds_char_t* const wl = (lds_char_t*)(wsm_);
+  lds_char_t* const xl = (lds_char_t*)(xsm_);
+
+  // Weight pieces of this thread: piece p = tid + 256 i -> row (tid >> 4) +
+  // 16 i, 16-byte column tid & 15 (rows past the selection read its last
+  // entry; their outputs are masked).
+  const char* w1 = static_cast<const char*>(a.w1t) + static_cast<size_t>(kbeg) * 2;
+  uint32_t woff[kUp1Loads];
+  int wdst[kUp1Loads];
+#pragma unroll
+  for (int i = 0; i < kUp1Loads; ++i) {
+    const int r = (tid >> 4) + 16 * i, col = tid & 15;
+    const int row = sel_row(a, min(n0 + r, n_sel - 1));
+    woff[i] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.d) * 2u + col * 16;
+    wdst[i] = r * kUpRowB + ((col ^ (r & 15)) * 16);
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  // x row of this lane (padding rows past B read row B - 1, as in the
+  // general form); this wave loads piece 4 wu + q4 of it.
+  const int b = b0 + c;
+  const bool xok = b < a.B;
+  const char* xsrc = static_cast<const char*>(a.x) +
+                     (static_cast<size_t>(xok ? b : a.B - 1) * a.d + kbeg + 8 * q4) * 2;
+  const int xrow = c * kUpRowB;
+
+  f32x4 acc[NBW];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](int st, UpW1& d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kUp1Loads; ++i) d.v[i] = ld16_stream(w1 + woff[i] + st * kUpRowB);
+  };
+  auto write_w = [&](int st, const UpW1& w) __attribute__((always_inline)) {
+    lds_char_t* const buf = wl + (st & 1) * (kUp1N * kUpRowB);
+#pragma unroll
+    for (int i = 0; i < kUp1Loads; ++i)
+      *(lds_u32x4_t*)(buf + wdst[i]) = __builtin_bit_cast(u32x4_t, w.v[i]);
+  };
+  auto load_x = [&](int st, UpX1& d) __attribute__((always_inline)) {
+    d.v[0] = ld16(xsrc + st * kUpRowB + wu * 64);
+  };
+  auto write_x = [&](int st, const UpX1& d) __attribute__((always_inline)) {
+    lds_char_t* const buf = xl + (st & 1) * (16 * kUpRowB);
+    const int piece = 4 * wu + q4;
+    *(lds_u32x4_t*)(buf + xrow + ((piece ^ c) * 16)) = __builtin_bit_cast(u32x4_t, d.v[0]);
+  };
+  // Step st: weights and x of st + 1 go from registers to LDS; x of st + 2
+  // is loaded into the x set just written, then the weights of st + 3 into
+  // the weight set just written; stage st is multiplied; one barrier closes
+  // the step (CHECK: only work inside the K range).
+  auto step = [&](int st, UpW1& wnext, UpX1& xr, auto check) __attribute__((always_inline)) {
+    constexpr bool C = decltype(check)::value;
+    if (!C || st + 1 < nst) {
+      write_w(st + 1, wnext);
+      write_x(st + 1, xr);
+    }
+    if (!C || st + 2 < nst) load_x(st + 2, xr);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!C || st + 3 < nst) load_w(st + 3, wnext);
+    const lds_char_t* const wbuf = wl + (st & 1) * (kUp1N * kUpRowB);
+    const lds_char_t* const xbuf = xl + (st & 1) * (16 * kUpRowB);
+#pragma unroll
+    for (int s = 0; s < kUpX; ++s) {
+      const int piece = 4 * s + q4;
+      const u32x4_t xv = *(const lds_u32x4_t*)(xbuf + xrow + ((piece ^ c) * 16));
+      const uint4 xb = __builtin_bit_cast(uint4, xv);
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int mb = NBW * wu + i;
+        const u32x4_t av = *(const lds_u32x4_t*)(wbuf + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
+        acc[i] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[i]);
+      }
+    }
+    __syncthreads();
+  };
+
+  if (nst > 0) {
+    // Unconditional prologue loads (short ranges load their last stage
+    // again), as in the general form.
+    UpW1 wa, wb;
+    UpX1 xr;
+    load_x(0, xr);
+    load_w(0, wa);
+    load_w(min(1, nst - 1), wb);
+    write_x(0, xr);
+    load_x(min(1, nst - 1), xr);
+    write_w(0, wa);
+    load_w(min(2, nst - 1), wa);
+    __syncthreads();
+    using Chk = std::true_type;
+    using NoChk = std::false_type;
+    int st = 0;
+    for (; st + 5 <= nst; st += 2) {
+      step(st, wb, xr, NoChk{});
+      step(st + 1, wa, xr, NoChk{});
+    }
+    for (; st + 2 <= nst; st += 2) {
+      step(st, wb, xr, Chk{});
+      step(st + 1, wa, xr, Chk{});
+    }
+    if (st < nst) step(st, wb, xr, Chk{});
+  }
+
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] for the batch block's 16 rows.
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    const int nbase = n0 + 16 * (NBW * wu + i) + 4 * q4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!sel_valid(a, nbase + r, n_sel)) acc[i][r] = 0.f;
+    if (a.up_splits == 1) {
+      const uint32_t lo = M::pack(fmaxf(acc[i][0], 0.f), fmaxf(acc[i][1], 0.f));
+      const uint32_t hi = M::pack(fmaxf(acc[i][2], 0.f), fmaxf(acc[i][3], 0.f));
+      *reinterpret_cast<uint2*>(static_cast<char*>(a.h) +
+                                (static_cast<size_t>(b) * a.n_pad + nbase) * 2) = make_uint2(lo, hi);
+    } else {
+      float* p = a.up_part + (static_cast<size_t>(split) * a.b_pad + b) * a.n_pad + nbase;
+      *reinterpret_cast<float4*>(p) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+  }
+}
+
+
 // H = relu(sum of the K-split partials), fixed order; one thread per 4
 // neurons of a computed row (rows 16 bb of each 64-row tile).  The splits'
 // loads are issued together (at most kMlpMaxUpSplits), then summed in order.
@@ -717,8 +882,12 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   const int dn_cols = 64 * a.dn_waves;
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
   const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
-  hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
-                     st, a);
+  if (BB == 1 && a.up_xlds)
+    hipLaunchKernelGGL((sha_mlp_up1_kernel<DT>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256),
+                       0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.up_splits > 1) {
