@@ -704,10 +704,12 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.n_pad = p.n_pad;
   a.b_pad = p.b_pad;
   a.bb = p.bb;
-  // One computed batch block: x shared through LDS by the up workgroup's
-  // waves (OPT-6.7B B = 16: 61.0-61.3 -> 59.3-59.6 us); SHA_MLP_UP_XLDS=0
-  // (a tuning hook) keeps each wave loading all of x.
-  a.up_xlds = p.bb == 1 && env_int("SHA_MLP_UP_XLDS", 1) != 0;
+  // One or two computed batch blocks: x shared through LDS by the up
+  // workgroup's waves (OPT-6.7B B = 16: 61.0-61.3 -> 59.3-59.6 us);
+  // SHA_MLP_UP_XLDS=0 (a tuning hook) keeps each wave loading all of its x,
+  // SHA_MLP_UP_XLDS=1 shares it for one batch block only.
+  const int xlds = env_int("SHA_MLP_UP_XLDS", 2);
+  a.up_xlds = (p.bb == 1 && xlds >= 1) || (p.bb == 2 && xlds >= 2);
   a.up_splits = p.up_splits;
   a.up_kper = p.up_kper;
   a.dn_splits = p.dn_splits;

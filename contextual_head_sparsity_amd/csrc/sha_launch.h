@@ -33,7 +33,7 @@ struct MlpArgs {
   int bb;               // 16-row batch blocks computed per 64-row tile: 1 (B <= 16),
                         // 2 (B <= 32) or 4; rows 16 bb .. 63 of a tile are never
                         // computed, read for an output row, or stored
-  int up_xlds;          // bb = 1: x shared through LDS by the up workgroup's waves
+  int up_xlds;          // bb <= 2: x shared through LDS by the up workgroup's waves
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
   int dn_waves;         // waves per down workgroup (64 output columns each): 4, or 8

@@ -458,31 +458,35 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   }
 }
 
-// One computed batch block (B <= 16): the four waves of the 128-neuron
-// workgroup all multiply the same 16 x rows, so instead of each loading all
-// of them, wave w loads piece column w of each row (one 16-byte piece per
-// lane per stage) two stages ahead, writes the pieces of stage st + 1 into
-// a double-buffered 16-row x tile in LDS (XOR-swizzled like the weights,
-// 2 x 4 KB), and every wave reads its B operands there: each x byte is read
-// from L2 once per workgroup instead of four times.  Weights move exactly
-// as in the general form; per neuron the products accumulate over the same
-// K stages in the same order, so its outputs are bit-identical.
+// One or two computed batch blocks (B <= 16, B <= 32): 4 / BB waves of the
+// 128-neuron workgroup multiply the same 16 x rows, so instead of each
+// loading all of them, the waves sharing a batch block split its piece
+// columns (BB 16-byte pieces per lane per stage each), load them two stages
+// ahead, write the pieces of stage st + 1 into a double-buffered 16 BB-row
+// x tile in LDS (XOR-swizzled like the weights, 2 x 4 BB KB), and every
+// wave reads its B operands there: each x byte is read from L2 once per
+// workgroup instead of 4 / BB times.  Weights move exactly as in the
+// general form; per neuron the products accumulate over the same K stages
+// in the same order, so its outputs are bit-identical.
 constexpr int kUp1N = kMlpUpNeurons;        // neurons per workgroup (128)
 constexpr int kUp1Loads = kUp1N * kUpPieces / 256;  // weight pieces per thread per stage
 
 struct UpW1 {
   uint4 v[kUp1Loads];
 };
-struct UpX1 {
-  uint4 v[1];
+template <int BB>
+struct UpXs {
+  uint4 v[BB];
 };
 
-template <int DT>
-__global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
+template <int DT, int BB>
+__global__ __launch_bounds__(256, 2) void sha_mlp_upx_kernel(MlpArgs a) {
   using M = Mx<DT>;
-  constexpr int NBW = 2;                      // neuron blocks per wave
+  static_assert(BB == 1 || BB == 2, "one or two batch blocks");
+  constexpr int NBW = 2 * BB;                 // neuron blocks per wave
+  using UpX1 = UpXs<BB>;
   __shared__ __attribute__((aligned(16))) char wsm_[2 * kUp1N * kUpRowB];
-  __shared__ __attribute__((aligned(16))) char xsm_[2 * 16 * kUpRowB];
+  __shared__ __attribute__((aligned(16))) char xsm_[2 * 16 * BB * kUpRowB];
   const int nblocks = a.n_pad / kUp1N;
   int t = blockIdx.x;
   const int nblk = t % nblocks;
@@ -516,13 +520,15 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
     wdst[i] = r * kUpRowB + ((col ^ (r & 15)) * 16);
   }
   const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wu / BB, bblk = wu % BB;    // neuron blocks grp * NBW .., batch block
   // x row of this lane (padding rows past B read row B - 1, as in the
-  // general form); this wave loads piece 4 wu + q4 of it.
-  const int b = b0 + c;
+  // general form); this wave loads pieces 4 s + q4 of it for
+  // s = grp * BB .. grp * BB + BB - 1.
+  const int b = b0 + 16 * bblk + c;
   const bool xok = b < a.B;
   const char* xsrc = static_cast<const char*>(a.x) +
                      (static_cast<size_t>(xok ? b : a.B - 1) * a.d + kbeg + 8 * q4) * 2;
-  const int xrow = c * kUpRowB;
+  const int xrow = (16 * bblk + c) * kUpRowB;
 
   f32x4 acc[NBW];
 #pragma unroll
@@ -539,12 +545,16 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
       *(lds_u32x4_t*)(buf + wdst[i]) = __builtin_bit_cast(u32x4_t, w.v[i]);
   };
   auto load_x = [&](int st, UpX1& d) __attribute__((always_inline)) {
-    d.v[0] = ld16(xsrc + st * kUpRowB + wu * 64);
+#pragma unroll
+    for (int j = 0; j < BB; ++j) d.v[j] = ld16(xsrc + st * kUpRowB + (grp * BB + j) * 64);
   };
   auto write_x = [&](int st, const UpX1& d) __attribute__((always_inline)) {
-    lds_char_t* const buf = xl + (st & 1) * (16 * kUpRowB);
-    const int piece = 4 * wu + q4;
-    *(lds_u32x4_t*)(buf + xrow + ((piece ^ c) * 16)) = __builtin_bit_cast(u32x4_t, d.v[0]);
+    lds_char_t* const buf = xl + (st & 1) * (16 * BB * kUpRowB);
+#pragma unroll
+    for (int j = 0; j < BB; ++j) {
+      const int piece = 4 * (grp * BB + j) + q4;
+      *(lds_u32x4_t*)(buf + xrow + ((piece ^ c) * 16)) = __builtin_bit_cast(u32x4_t, d.v[j]);
+    }
   };
   // Step st: weights and x of st + 1 go from registers to LDS; x of st + 2
   // is loaded into the x set just written, then the weights of st + 3 into
@@ -560,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     if (!C || st + 3 < nst) load_w(st + 3, wnext);
     const lds_char_t* const wbuf = wl + (st & 1) * (kUp1N * kUpRowB);
-    const lds_char_t* const xbuf = xl + (st & 1) * (16 * kUpRowB);
+    const lds_char_t* const xbuf = xl + (st & 1) * (16 * BB * kUpRowB);
 #pragma unroll
     for (int s = 0; s < kUpX; ++s) {
       const int piece = 4 * s + q4;
@@ -568,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
       const uint4 xb = __builtin_bit_cast(uint4, xv);
 #pragma unroll
       for (int i = 0; i < NBW; ++i) {
-        const int mb = NBW * wu + i;
+        const int mb = NBW * grp + i;
         const u32x4_t av = *(const lds_u32x4_t*)(wbuf + (16 * mb + c) * kUpRowB + ((piece ^ c) * 16));
         acc[i] = M::mma(__builtin_bit_cast(uint4, av), xb, acc[i]);
       }
@@ -603,10 +613,11 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up1_kernel(MlpArgs a) {
     if (st < nst) step(st, wb, xr, Chk{});
   }
 
-  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b] for the batch block's 16 rows.
+  // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b]: the computed rows of the
+  // tile (16 BB of its 64).
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
-    const int nbase = n0 + 16 * (NBW * wu + i) + 4 * q4;
+    const int nbase = n0 + 16 * (NBW * grp + i) + 4 * q4;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (!sel_valid(a, nbase + r, n_sel)) acc[i][r] = 0.f;
@@ -882,9 +893,9 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   const int dn_cols = 64 * a.dn_waves;
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
   const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
-  if (BB == 1 && a.up_xlds)
-    hipLaunchKernelGGL((sha_mlp_up1_kernel<DT>), dim3(static_cast<unsigned>(up_wgs)), dim3(256), 0,
-                       st, a);
+  if (BB <= 2 && a.up_xlds)
+    hipLaunchKernelGGL((sha_mlp_upx_kernel<DT, BB <= 2 ? BB : 1>), dim3(static_cast<unsigned>(up_wgs)),
+                       dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256),
                        0, st, a);
