@@ -411,7 +411,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
 // selective MLP planning
 // ---------------------------------------------------------------------------
 struct MlpPlan {
-  int n_pad, b_pad, bb, up_splits, up_kper, dn_splits, dn_waves;
+  int n_pad, b_pad, bb, up_nu, up_splits, up_kper, dn_splits, dn_waves;
   size_t h_bytes, up_bytes, dn_bytes;
 };
 
@@ -448,8 +448,27 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   p.n_pad = ((n_max > 0 ? n_max : 1) + NU - 1) / NU * NU;
   p.b_pad = (B + 63) / 64 * 64;
   p.bb = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-  const long long up_items = static_cast<long long>(p.n_pad / NU) * (p.b_pad / 64);
   const int kstages = d / sha::kMlpUpKc;
+  // Up tile: 128 neurons, or for full batch tiles 144 when that leaves
+  // fewer idle slots in the grid's last round of resident workgroups
+  // (OPT-66B: 256 tiles x 2 splits = 512 workgroups, one round, against
+  // 288 x 2 = 576 with 128); SHA_MLP_UP_TILE = 128 or 144 forces one (a
+  // tuning hook).
+  p.up_nu = NU;
+  if (p.bb == 4) {
+    const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
+    auto idle = [&](int nu) {
+      const long long items = static_cast<long long>((p.n_pad + nu - 1) / nu) * (p.b_pad / 64);
+      const long long wgs = items * up_split_count(items, kstages, cus);
+      const long long rounds = (wgs + slots - 1) / slots;
+      return rounds * slots - wgs;
+    };
+    if (idle(144) < idle(NU)) p.up_nu = 144;
+    const int tile = env_int("SHA_MLP_UP_TILE", 0);
+    if (tile == 128 || tile == 144) p.up_nu = tile;
+  }
+  const long long up_items =
+      static_cast<long long>((p.n_pad + p.up_nu - 1) / p.up_nu) * (p.b_pad / 64);
   int us = up_split_count(up_items, kstages, cus);
   if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
   if (us > sha::kMlpMaxUpSplits) us = sha::kMlpMaxUpSplits;
@@ -680,7 +699,7 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   // Both products launch 1-D grids: their workgroup counts must fit one
   // grid dimension (and an int in the kernels).
   const long long btiles = p.b_pad / 64;
-  if (static_cast<long long>(p.n_pad / sha::kMlpUpNeurons) * p.up_splits * btiles > 0x7FFFFFFFLL ||
+  if (static_cast<long long>((p.n_pad + p.up_nu - 1) / p.up_nu) * p.up_splits * btiles > 0x7FFFFFFFLL ||
       static_cast<long long>(d / 256) * p.dn_splits * btiles > 0x7FFFFFFFLL)
     return SHA_ERR_INVALID_ARG;
   const size_t need = p.h_bytes + p.up_bytes + p.dn_bytes;
@@ -704,6 +723,7 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.n_pad = p.n_pad;
   a.b_pad = p.b_pad;
   a.bb = p.bb;
+  a.up_nu = p.up_nu;
   // One or two computed batch blocks: x shared through LDS by the up
   // workgroup's waves (OPT-6.7B B = 16: 61.0-61.3 -> 59.3-59.6 us);
   // SHA_MLP_UP_XLDS=0 (a tuning hook) keeps each wave loading all of its x,

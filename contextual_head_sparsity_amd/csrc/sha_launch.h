@@ -34,6 +34,7 @@ struct MlpArgs {
                         // 2 (B <= 32) or 4; rows 16 bb .. 63 of a tile are never
                         // computed, read for an output row, or stored
   int up_xlds;          // bb <= 2: x shared through LDS by the up workgroup's waves
+  int up_nu;            // neurons per up workgroup: 128, or 144 (bb = 4)
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
   int dn_waves;         // waves per down workgroup (64 output columns each): 4, or 8

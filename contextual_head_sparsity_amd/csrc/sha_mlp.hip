@@ -300,24 +300,35 @@ constexpr int kUpLoads = kUpN * kUpPieces / 256;  // weight pieces per thread pe
 constexpr int kUpX = kUpKc / 32;            // x pieces (MFMA K steps) per lane per stage
 static_assert(kUpPieces == 16, "the swizzle and the row mapping assume 16 pieces per row");
 
-struct UpW {
-  uint4 v[kUpLoads];
+template <int L>
+struct UpWn {
+  uint4 v[L];
 };
+using UpW = UpWn<kUpLoads>;
 struct UpX {
   uint4 v[kUpX];
 };
 
 // BB = 16-row batch blocks computed per 64-row tile (1 for B <= 16, 2 for
-// B <= 32, else 4).  The four waves split the tile's 8 neuron blocks into
-// 4 / BB groups: wave w multiplies neuron blocks of group w / BB by batch
-// block w % BB, so no wave multiplies padding rows of a small batch.
-template <int DT, int BB>
+// B <= 32, else 4).  The four waves split the tile's NU / 16 neuron blocks
+// into 4 / BB groups: wave w multiplies neuron blocks of group w / BB by
+// batch block w % BB, so no wave multiplies padding rows of a small batch.
+// NU = neurons per workgroup: 128, or 144 for full batch tiles where that
+// fills whole rounds of workgroups (OPT-66B: 36864 / 144 = 256 tiles, two
+// K splits, exactly one round at two per CU; 128 leaves a 1.125-round
+// grid); a last tile past n_pad stores nothing there.
+template <int DT, int BB, int NU>
 __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
   static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
+  static_assert(NU % 16 == 0 && (NU / 16) * BB % 4 == 0, "whole neuron blocks per wave");
+  constexpr int kUpN = NU;                    // neurons per workgroup
+  constexpr int kUpNB = kUpN / 16;            // MFMA neuron blocks
+  constexpr int kUpLoads = kUpN * kUpPieces / 256;  // weight pieces per thread per stage
+  using UpW = UpWn<kUpLoads>;
   constexpr int NBW = kUpNB * BB / 4;         // neuron blocks per wave
   __shared__ __attribute__((aligned(16))) char wsm_[2 * kUpN * kUpRowB];
-  const int nblocks = a.n_pad / kUpN;
+  const int nblocks = (a.n_pad + kUpN - 1) / kUpN;
   int t = blockIdx.x;
   const int nblk = t % nblocks;
   t /= nblocks;
@@ -442,6 +453,7 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int nbase = n0 + 16 * (grp * NBW + i) + 4 * q4;
+    if (nbase >= a.n_pad) continue;             // a last tile past the padding
     // Entries outside [0, D) (and past the count) produce no activation.
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -892,13 +904,17 @@ template <int DT, int BB>
 hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   const int dn_cols = 64 * a.dn_waves;
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
-  const long long up_wgs = static_cast<long long>(a.n_pad / kUpN) * a.up_splits * btiles;
+  const long long up_wgs =
+      static_cast<long long>((a.n_pad + a.up_nu - 1) / a.up_nu) * a.up_splits * btiles;
   if (BB <= 2 && a.up_xlds)
     hipLaunchKernelGGL((sha_mlp_upx_kernel<DT, BB <= 2 ? BB : 1>), dim3(static_cast<unsigned>(up_wgs)),
                        dim3(256), 0, st, a);
+  else if (BB == 4 && a.up_nu == 144)
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, 4, 144>), dim3(static_cast<unsigned>(up_wgs)),
+                       dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB>), dim3(static_cast<unsigned>(up_wgs)), dim3(256),
-                       0, st, a);
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB, 128>), dim3(static_cast<unsigned>(up_wgs)),
+                       dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.up_splits > 1) {

@@ -113,6 +113,35 @@ def test_up_shared_x_agrees(B, d, D, k_row, monkeypatch):
     assert torch.equal(wl.raw_bits(outs["0"]), wl.raw_bits(outs["2"]))
 
 
+@pytest.mark.parametrize("B,d,D,k_row", [(64, 1024, 36864, 3686), (40, 512, 2000, 150),
+                                         (70, 256, 900, 60), (33, 768, 5000, 40)])
+def test_up_tiles_agree(B, d, D, k_row, monkeypatch):
+    """Full batch tiles: 128- and 144-neuron up workgroups give bit-identical
+    outputs at the same K split count (per neuron the same stages in the
+    same order) and both match the oracle; the shapes include selections
+    whose last 144-neuron tile runs past the padding."""
+    say(f"[mlp] up tiles B={B} d={d} D={D} k_row={k_row}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 13 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    outs = {}
+    for splits in ("2", None):
+        for tile in ("128", "144"):
+            monkeypatch.setenv("SHA_MLP_UP_TILE", tile)
+            if splits:
+                monkeypatch.setenv("SHA_MLP_UP_SPLITS", splits)
+            else:
+                monkeypatch.delenv("SHA_MLP_UP_SPLITS", raising=False)
+            y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+            torch.cuda.synchronize()
+            err = float(np.abs(y.cpu().double().numpy() - ref).max())
+            assert err <= _tol("bf16", ref), (tile, splits, err)
+            outs[(splits, tile)] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs[("2", "128")]), wl.raw_bits(outs[("2", "144")]))
+
+
 def test_union_rows_not_16_byte_aligned():
     """Row lists need only 4-byte alignment (here 4 bytes past a 16-byte
     boundary)."""
