@@ -114,7 +114,8 @@ def test_up_shared_x_agrees(B, d, D, k_row, monkeypatch):
 
 
 @pytest.mark.parametrize("B,d,D,k_row", [(64, 1024, 36864, 3686), (40, 512, 2000, 150),
-                                         (70, 256, 900, 60), (33, 768, 5000, 40)])
+                                         (70, 256, 900, 60), (33, 768, 5000, 40),
+                                         (40, 256, 100, 30)])
 def test_up_tiles_agree(B, d, D, k_row, monkeypatch):
     """Full batch tiles: 128- and 144-neuron up workgroups give bit-identical
     outputs at the same K split count (per neuron the same stages in the
