@@ -17,21 +17,25 @@
 //            Up to 8192 row entries, one workgroup does all of it with the
 //            flags as LDS bits (one launch).
 //   up     - H^T = W1t[S] x^T on MFMA (v_mfma_f32_16x16x32, 16-bit inputs):
-//            a workgroup owns 128 selected neurons x 64 batch rows over a K
-//            range; weight rows stream in 256-byte runs (non-temporal
-//            128-bit loads, three stages ahead) through swizzled LDS into A
-//            operands, x pieces come from L2 as B operands.  With one K
-//            split it applies ReLU and writes H (16-bit); with several it
-//            writes fp32 partials and `up_finalize` sums them.
-//   down   - y = H W2t[S] on MFMA: a workgroup owns 64 batch rows x 256
-//            output columns over a range of the selected neurons; the
+//            a workgroup owns 128 selected neurons (144 for full batch
+//            tiles when that makes whole rounds of resident workgroups) x
+//            64 batch rows over a K range; weight rows stream in 256-byte
+//            runs (non-temporal 128-bit loads, three stages ahead) through
+//            swizzled LDS into A operands, x pieces come from L2 as B
+//            operands.  With one K split it applies ReLU and writes H
+//            (16-bit); with several it writes fp32 partials and
+//            `up_finalize` sums them.
+//   down   - y = H W2t[S] on MFMA: a workgroup of 8 waves owns 64 batch
+//            rows x 512 output columns (4 waves x 256 columns when d is not
+//            a multiple of 512) over a range of the selected neurons; the
 //            gathered W2t rows are staged in LDS and read back transposed
 //            (ds_read_b64_tr_b16) as B operands, H comes from LDS as A.
 //            Split ranges of neurons write fp32 partials that
 //            `down_finalize` sums in a fixed order.
 //   Batches of at most 16 (32) rows compute only the 1 (2) batch blocks of
 //   16 rows that hold rows: in the up projection the waves then split the
-//   tile's neurons instead of its batch blocks.
+//   tile's neurons instead of its batch blocks, and the waves sharing a
+//   batch block share its x through LDS (`sha_mlp_upx_kernel`).
 // The selection count is read on the device, so union -> up -> down needs no
 // host synchronisation; grids are sized for the caller's upper bound n_max
 // and workgroups past the actual count exit or mask.
