@@ -734,6 +734,10 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.up_kper = p.up_kper;
   a.dn_splits = p.dn_splits;
   a.dn_waves = p.dn_waves;
+  // Split partials through LDS as whole-row pieces (down kernel 130.5 ->
+  // 126.8 us at OPT-66B B = 64); SHA_MLP_DN_STAGE=0 (a tuning hook) keeps
+  // the direct 4-byte stores.
+  a.dn_stage = env_int("SHA_MLP_DN_STAGE", 1) != 0;
   (void)hipGetLastError();
   const hipError_t e = sha::launch_selective_mlp(a, dtype, stream);
   if (e != hipSuccess) {

@@ -37,6 +37,7 @@ struct MlpArgs {
   int up_nu;            // neurons per up workgroup: 128, or 144 (bb = 4)
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
+  int dn_stage;         // down split partials stored through LDS as whole-row pieces
   int dn_waves;         // waves per down workgroup (64 output columns each): 4, or 8
                         // when d is a multiple of 512
 };

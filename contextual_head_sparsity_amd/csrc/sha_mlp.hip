@@ -64,6 +64,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) float lds_float_t;
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -858,21 +859,63 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
   }
 
   // lane holds y[b = b0 + 16 mb + 4 q4 + r][col = col0 + 64 wave + 16 nb + c]
+  if (a.dn_splits == 1 || !a.dn_stage) {
 #pragma unroll
-  for (int mb = 0; mb < BB; ++mb)
+    for (int mb = 0; mb < BB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int b = b0 + 16 * mb + 4 * q4 + r;
-      if (b >= a.B) continue;
+      for (int r = 0; r < 4; ++r) {
+        const int b = b0 + 16 * mb + 4 * q4 + r;
+        if (b >= a.B) continue;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int col = col0 + 64 * wave + 16 * nb + c;
-        if (a.dn_splits == 1)
-          Elem<DT>::store(a.y, static_cast<size_t>(b) * a.d + col, acc[mb][nb][r]);
-        else
-          a.dn_part[(static_cast<size_t>(split) * a.b_pad + b) * a.d + col] = acc[mb][nb][r];
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = col0 + 64 * wave + 16 * nb + c;
+          if (a.dn_splits == 1)
+            Elem<DT>::store(a.y, static_cast<size_t>(b) * a.d + col, acc[mb][nb][r]);
+          else
+            a.dn_part[(static_cast<size_t>(split) * a.b_pad + b) * a.d + col] = acc[mb][nb][r];
+        }
+      }
+    return;
+  }
+  // fp32 split partials: every workgroup of the (one-round) grid reaches
+  // this point at about the same time, so the stores are one burst.  They
+  // go through the weight tile in LDS, up to 32 rows at a time, and leave
+  // as 16-byte pieces of whole rows (a wave writes 1 KB contiguous) instead
+  // of 4-byte stores in 64-byte row segments.
+  constexpr int kRows = 16 * BB < 32 ? 16 * BB : 32;      // rows per pass
+  constexpr int kPitch = kDnCols * 4 + 16;                // bytes per staged row
+  static_assert(kRows * kPitch <= kDnKc * kDnWPitch, "staged rows fit the weight tile");
+  float* const pout = a.dn_part + static_cast<size_t>(split) * a.b_pad * a.d;
+#pragma unroll
+  for (int pass = 0; pass < (16 * BB) / kRows; ++pass) {
+    __syncthreads();  // the last products' (or the previous pass's) LDS reads are done
+#pragma unroll
+    for (int mb = 0; mb < BB; ++mb) {
+      if (mb * 16 / kRows != pass) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mb + 4 * q4 + r - pass * kRows;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          *(lds_float_t*)(wl + row * kPitch + (64 * wave + 16 * nb + c) * 4) = acc[mb][nb][r];
       }
     }
+    __syncthreads();
+    constexpr int kPieces = kRows * kDnCols / 4;         // 16-byte pieces of the pass
+#pragma unroll
+    for (int i = 0; i < (kPieces + T - 1) / T; ++i) {
+      const int idx = tid + T * i;
+      if (idx < kPieces) {
+        const int row = idx / (kDnCols / 4), piece = idx % (kDnCols / 4);
+        const int b = b0 + pass * kRows + row;
+        if (b < a.B) {
+          const u32x4_t v = *(const lds_u32x4_t*)(wl + row * kPitch + piece * 16);
+          *reinterpret_cast<uint4*>(pout + static_cast<size_t>(b) * a.d + col0 + piece * 4) =
+              __builtin_bit_cast(uint4, v);
+        }
+      }
+    }
+  }
 }
 
 // y = sum of the neuron-split partials, fixed order; one thread per 4

@@ -143,6 +143,33 @@ def test_up_tiles_agree(B, d, D, k_row, monkeypatch):
     assert torch.equal(wl.raw_bits(outs[("2", "128")]), wl.raw_bits(outs[("2", "144")]))
 
 
+@pytest.mark.parametrize("B,d,D,k_row,waves", [(64, 1024, 3000, 200, "8"), (64, 768, 3000, 200, "4"),
+                                               (70, 512, 2000, 150, "8"), (16, 4096, 16384, 1638, "8"),
+                                               (20, 1024, 1500, 60, "8"), (5, 768, 1000, 100, "4")])
+def test_down_staged_partials_agree(B, d, D, k_row, waves, monkeypatch):
+    """The down kernel's split partials stored through LDS as whole-row
+    pieces give bit-identical outputs to the direct stores (4- and 8-wave
+    workgroups, one to four batch blocks, two batch tiles, partial rows past
+    B) and match the oracle."""
+    say(f"[mlp] staged partials B={B} d={d} D={D} k_row={k_row} waves={waves}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 19 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    monkeypatch.setenv("SHA_MLP_DN_WAVES", waves)
+    monkeypatch.setenv("SHA_MLP_DN_SPLITS", "3")
+    outs = {}
+    for stage in ("0", "1"):
+        monkeypatch.setenv("SHA_MLP_DN_STAGE", stage)
+        y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+        torch.cuda.synchronize()
+        err = float(np.abs(y.cpu().double().numpy() - ref).max())
+        assert err <= _tol("bf16", ref), (stage, err)
+        outs[stage] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs["0"]), wl.raw_bits(outs["1"]))
+
+
 def test_union_rows_not_16_byte_aligned():
     """Row lists need only 4-byte alignment (here 4 bytes past a 16-byte
     boundary)."""
