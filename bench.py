@@ -447,7 +447,9 @@ def summarize_traffic(args):
 
 def bench_mlp(args):
     """Selective MLP (device union + up/down projections) on one GPU: time per
-    layer call and effective GB/s on the selected neurons' weight rows."""
+    layer call and effective GB/s on the selected neurons' weight rows, over
+    back-to-back calls from Python (the value) and as device time per call
+    with the calls captured in a HIP graph (`graph`)."""
     w = wl.MLP_WORKLOADS[args.mlp]
     if args.mlp_batch:
         w = w.with_(B=args.mlp_batch)
@@ -485,6 +487,21 @@ def bench_mlp(args):
         sha.selective_mlp(x, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd, stream=stream)
 
     dms, _ = time_calls(dcall, args.steps, args.warmup, stream)
+    # The same calls captured in a HIP graph (no launch gaps between the
+    # union's and the MLP's kernels): device time per call.
+    cur = lambda: torch.cuda.current_stream(dev)
+
+    def gcall(i):
+        sha.mlp_union(rows, w.D, sel=sel, n_sel=n_sel, stream=cur(), workspace=uws)
+        a, b = ws[i % copies]
+        sha.selective_mlp(x, a, b, sel, n_sel, n_max=n_max, out=y, workspace=work, stream=cur())
+
+    def gdcall(i):
+        a, b = ws[i % copies]
+        sha.selective_mlp(x, a, b, sel_all, n_all, n_max=w.D, out=y, workspace=wsd, stream=cur())
+
+    g_us = graph_us_per_call(gcall, 20, dev, 2, 5)
+    gd_us = graph_us_per_call(gdcall, 20, dev, 2, 5)
     wbytes = n * w.weight_bytes_per_neuron
     out = {"metric": f"selective MLP \u00b5s/layer + effective weight GB/s, {w.name}",
            "value": round(wbytes / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
@@ -498,6 +515,12 @@ def bench_mlp(args):
                         "frac": round(wbytes / (float(np.mean(ev)) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                         "launch_avg_us": round(float(np.mean(ev)) * 1e3, 2),
                         "note": "event span covers union + up + down (+ finalize) kernels"},
+           "graph": {"us_per_layer": round(g_us, 2),
+                     "weight_GBps": round(wbytes / (g_us / 1e6) / 1e9, 2),
+                     "pct_hbm_peak": round(100 * wbytes / (g_us / 1e6) / 1e9 / HBM_PEAK_GBS, 2),
+                     "all_neurons_us": round(gd_us, 2),
+                     "speedup_selective_vs_all": round(gd_us / g_us, 3),
+                     "note": "20 calls captured in a HIP graph, replayed: device time per call"},
            "all_neurons": {"us_per_layer": round(dms * 1e3, 2),
                            "GBps": round(w.D * w.weight_bytes_per_neuron / (dms / 1e3) / 1e9, 2),
                            "speedup_selective_vs_all": round(dms / ms, 3),
@@ -937,7 +960,10 @@ def extras(args):
                      "us_per_layer": r["us_per_layer"], "weight_GBps": r["value"],
                      "pct_hbm_peak": r["pct_hbm_peak"], "all_neurons_us": a["us_per_layer"],
                      "speedup_vs_all_neurons": a["speedup_selective_vs_all"],
-                     "ideal_speedup": a["ideal_speedup"]}
+                     "ideal_speedup": a["ideal_speedup"],
+                     "graph_us_per_layer": r["graph"]["us_per_layer"],
+                     "graph_pct_hbm_peak": r["graph"]["pct_hbm_peak"],
+                     "graph_speedup_vs_all_neurons": r["graph"]["speedup_selective_vs_all"]}
         torch.cuda.empty_cache()
     router = {}
     for name, w in wl.WORKLOADS.items():

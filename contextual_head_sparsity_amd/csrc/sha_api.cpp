@@ -724,6 +724,10 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.b_pad = p.b_pad;
   a.bb = p.bb;
   a.up_nu = p.up_nu;
+  // K-split partials through LDS as whole-row pieces (OPT-66B B = 64, union
+  // + MLP in a graph: 252.8-255.6 -> 247.6-250.4 us); SHA_MLP_UP_STAGE=0
+  // (a tuning hook) keeps the direct float4 stores.
+  a.up_stage = env_int("SHA_MLP_UP_STAGE", 1) != 0;
   // One or two computed batch blocks: x shared through LDS by the up
   // workgroup's waves (OPT-6.7B B = 16: 61.0-61.3 -> 59.3-59.6 us);
   // SHA_MLP_UP_XLDS=0 (a tuning hook) keeps each wave loading all of its x,

@@ -455,6 +455,41 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
 
   // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b]: the computed rows of the
   // tile (16 BB of its 64).
+  if (a.up_splits > 1 && a.up_stage) {
+    // fp32 K-split partials of a one-round grid leave in one burst: through
+    // the weight tile in LDS as 16-byte pieces of whole rows (NU neurons of
+    // one batch row contiguous) instead of float4 stores in 64-byte segments.
+    constexpr int kPitch = kUpN * 4 + 16;     // bytes per staged row
+    static_assert(16 * BB * kPitch <= 2 * kUpN * kUpRowB, "staged rows fit the weight tile");
+    __syncthreads();                          // the last stage's LDS reads are done
+    const int row = 16 * (wu % BB) + c;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const int nl = 16 * (grp * NBW + i) + 4 * q4;
+      float4 v = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      if (!sel_valid(a, n0 + nl, n_sel)) v.x = 0.f;
+      if (!sel_valid(a, n0 + nl + 1, n_sel)) v.y = 0.f;
+      if (!sel_valid(a, n0 + nl + 2, n_sel)) v.z = 0.f;
+      if (!sel_valid(a, n0 + nl + 3, n_sel)) v.w = 0.f;
+      *(lds_u32x4_t*)(wl + row * kPitch + nl * 4) = __builtin_bit_cast(u32x4_t, v);
+    }
+    __syncthreads();
+    constexpr int kQuads = kUpN / 4;          // 16-byte pieces per row
+    float* const base = a.up_part + (static_cast<size_t>(split) * a.b_pad + b0) * a.n_pad + n0;
+#pragma unroll
+    for (int i = 0; i < (16 * BB * kQuads + 255) / 256; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < 16 * BB * kQuads) {
+        const int rr = idx / kQuads, q = idx % kQuads;
+        if (n0 + 4 * q < a.n_pad) {
+          const u32x4_t v = *(const lds_u32x4_t*)(wl + rr * kPitch + q * 16);
+          *reinterpret_cast<uint4*>(base + static_cast<size_t>(rr) * a.n_pad + 4 * q) =
+              __builtin_bit_cast(uint4, v);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     const int nbase = n0 + 16 * (grp * NBW + i) + 4 * q4;

@@ -170,6 +170,33 @@ def test_down_staged_partials_agree(B, d, D, k_row, waves, monkeypatch):
     assert torch.equal(wl.raw_bits(outs["0"]), wl.raw_bits(outs["1"]))
 
 
+@pytest.mark.parametrize("B,d,D,k_row,tile", [(64, 1024, 36864, 3686, "144"), (64, 1024, 3000, 200, "128"),
+                                              (70, 512, 2000, 150, "144"), (40, 256, 100, 30, "144"),
+                                              (33, 768, 5000, 40, "128")])
+def test_up_staged_partials_agree(B, d, D, k_row, tile, monkeypatch):
+    """Full batch tiles: the up kernel's K-split partials stored through LDS
+    as whole-row pieces give bit-identical outputs to the direct stores
+    (128- and 144-neuron tiles, a last tile past the padding, two batch
+    tiles, rows past B) and match the oracle."""
+    say(f"[mlp] up staged partials B={B} d={d} D={D} k_row={k_row} tile={tile}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 23 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    monkeypatch.setenv("SHA_MLP_UP_TILE", tile)
+    monkeypatch.setenv("SHA_MLP_UP_SPLITS", "2")
+    outs = {}
+    for stage in ("0", "1"):
+        monkeypatch.setenv("SHA_MLP_UP_STAGE", stage)
+        y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+        torch.cuda.synchronize()
+        err = float(np.abs(y.cpu().double().numpy() - ref).max())
+        assert err <= _tol("bf16", ref), (stage, err)
+        outs[stage] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs["0"]), wl.raw_bits(outs["1"]))
+
+
 def test_union_rows_not_16_byte_aligned():
     """Row lists need only 4-byte alignment (here 4 bytes past a 16-byte
     boundary)."""
