@@ -411,7 +411,7 @@ sha_status run(const Problem& p, int nsplit_req, void* ws, size_t ws_bytes, hipS
 // selective MLP planning
 // ---------------------------------------------------------------------------
 struct MlpPlan {
-  int n_pad, b_pad, bb, up_nu, up_splits, up_kper, dn_splits, dn_waves;
+  int n_pad, b_pad, bb, up_nu, up_kg, up_splits, up_kper, dn_splits, dn_waves;
   size_t h_bytes, up_bytes, dn_bytes;
 };
 
@@ -454,22 +454,49 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   // (OPT-66B: 256 tiles x 2 splits = 512 workgroups, one round, against
   // 288 x 2 = 576 with 128); SHA_MLP_UP_TILE = 128 or 144 forces one (a
   // tuning hook).
+  //
+  // Two K groups per up workgroup (8 waves, one workgroup per CU, the halves
+  // of K summed on chip) replace K splits for full batch tiles whose tiles
+  // alone make about a round at one per CU while the four-wave form would
+  // split K (OPT-66B: 256 tiles of 144 neurons, no fp32 partials and no
+  // finalize); the tile is then the one with fewer idle CUs in the last
+  // round.  SHA_MLP_UP_KG = 1 or 2 forces one form (2 where d / 128 is even;
+  // a tuning hook); SHA_MLP_UP_SPLITS keeps the four-wave form.
   p.up_nu = NU;
+  p.up_kg = 1;
   if (p.bb == 4) {
-    const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
-    auto idle = [&](int nu) {
-      const long long items = static_cast<long long>((p.n_pad + nu - 1) / nu) * (p.b_pad / 64);
-      const long long wgs = items * up_split_count(items, kstages, cus);
-      const long long rounds = (wgs + slots - 1) / slots;
-      return rounds * slots - wgs;
+    auto items_of = [&](int nu) {
+      return static_cast<long long>((p.n_pad + nu - 1) / nu) * (p.b_pad / 64);
     };
-    if (idle(144) < idle(NU)) p.up_nu = 144;
+    auto kg2_fits = [&](int nu) {
+      const long long items = items_of(nu);
+      return items * 100 >= 95LL * cus && up_split_count(items, kstages, cus) >= 2;
+    };
+    const int kg_env = env_int("SHA_MLP_UP_KG", 0);
+    if (kstages % 2 == 0 && env_int("SHA_MLP_UP_SPLITS", 0) <= 0 && kg_env != 1 &&
+        (kg_env == 2 || kg2_fits(NU) || kg2_fits(144))) {
+      p.up_kg = 2;
+      auto idle = [&](int nu) {
+        const long long items = items_of(nu);
+        return (items + cus - 1) / cus * cus - items;
+      };
+      if (idle(144) < idle(NU)) p.up_nu = 144;
+    } else {
+      const long long slots = static_cast<long long>(kUpWgsPerCu) * cus;
+      auto idle = [&](int nu) {
+        const long long items = items_of(nu);
+        const long long wgs = items * up_split_count(items, kstages, cus);
+        const long long rounds = (wgs + slots - 1) / slots;
+        return rounds * slots - wgs;
+      };
+      if (idle(144) < idle(NU)) p.up_nu = 144;
+    }
     const int tile = env_int("SHA_MLP_UP_TILE", 0);
     if (tile == 128 || tile == 144) p.up_nu = tile;
   }
   const long long up_items =
       static_cast<long long>((p.n_pad + p.up_nu - 1) / p.up_nu) * (p.b_pad / 64);
-  int us = up_split_count(up_items, kstages, cus);
+  int us = p.up_kg == 2 ? 1 : up_split_count(up_items, kstages, cus);
   if (env_int("SHA_MLP_UP_SPLITS", 0) > 0) us = env_int("SHA_MLP_UP_SPLITS", 0);  // tuning hook
   if (us > sha::kMlpMaxUpSplits) us = sha::kMlpMaxUpSplits;
   if (us > kstages) us = kstages;
@@ -724,6 +751,7 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   a.b_pad = p.b_pad;
   a.bb = p.bb;
   a.up_nu = p.up_nu;
+  a.up_kg = p.up_kg;
   // K-split partials through LDS as whole-row pieces (OPT-66B B = 64, union
   // + MLP in a graph: 252.8-255.6 -> 247.6-250.4 us); SHA_MLP_UP_STAGE=0
   // (a tuning hook) keeps the direct float4 stores.

@@ -36,6 +36,8 @@ struct MlpArgs {
   int up_xlds;          // bb <= 2: x shared through LDS by the up workgroup's waves
   int up_nu;            // neurons per up workgroup: 128, or 144 (bb = 4)
   int up_stage;         // up split partials stored through LDS as whole-row pieces
+  int up_kg;            // K groups per up workgroup: 1, or 2 (bb = 4, one K split,
+                        // an even stage count; 512 threads)
   int up_splits, up_kper;  // K splits of the up projection and K elements per split
   int dn_splits;        // neuron-range splits of the down projection
   int dn_stage;         // down split partials stored through LDS as whole-row pieces

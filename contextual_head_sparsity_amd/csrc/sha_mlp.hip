@@ -24,7 +24,9 @@
 //            swizzled LDS into A operands, x pieces come from L2 as B
 //            operands.  With one K split it applies ReLU and writes H
 //            (16-bit); with several it writes fp32 partials and
-//            `up_finalize` sums them.
+//            `up_finalize` sums them.  Full batch tiles whose grid is about
+//            one round at one workgroup per CU take 512 threads in two K
+//            groups instead of K splits: the halves of K are summed on chip.
 //   down   - y = H W2t[S] on MFMA: a workgroup of 8 waves owns 64 batch
 //            rows x 512 output columns (4 waves x 256 columns when d is not
 //            a multiple of 512) over a range of the selected neurons; the
@@ -297,7 +299,6 @@ __device__ __forceinline__ bool sel_valid(const MlpArgs& a, int n, int count) {
 // younger weight stages in flight (loads complete in order).
 // Workgroup id = ((btile * up_splits) + split) * nblocks + nblock.
 constexpr int kUpN = kMlpUpNeurons;         // neurons per workgroup
-constexpr int kUpNB = kUpN / 16;            // MFMA neuron blocks
 constexpr int kUpKc = kMlpUpKc;             // k per stage
 constexpr int kUpRowB = kUpKc * 2;          // bytes of one weight row per stage
 constexpr int kUpPieces = kUpRowB / 16;     // 16-byte pieces per row per stage
@@ -322,17 +323,30 @@ struct UpX {
 // fills whole rounds of workgroups (OPT-66B: 36864 / 144 = 256 tiles, two
 // K splits, exactly one round at two per CU; 128 leaves a 1.125-round
 // grid); a last tile past n_pad stores nothing there.
-template <int DT, int BB, int NU>
-__global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
+//
+// KG = K groups per workgroup: 1, or 2 (512 threads, one workgroup per CU):
+// two sets of four waves, each the four-wave form above with its own LDS
+// tiles, multiply the first and the second half of the stages, and the
+// halves are summed on chip ((0 + first) + second, the order in which the
+// two-split finalize sums them, so H is bit-identical to that form) and H
+// leaves as 16-byte pieces of whole rows.  For full batch tiles whose
+// grid is one round at one workgroup per CU (OPT-66B: 256 tiles of 144
+// neurons), this replaces two K splits: no fp32 partials go through HBM and
+// no finalize launch follows.  The host takes it only with one K split and
+// an even stage count (d / 128 is even for every d it accepts).
+template <int DT, int BB, int NU, int KG>
+__global__ __launch_bounds__(256 * KG, 2 / KG) void sha_mlp_up_kernel(MlpArgs a) {
   using M = Mx<DT>;
   static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
   static_assert(NU % 16 == 0 && (NU / 16) * BB % 4 == 0, "whole neuron blocks per wave");
+  static_assert(KG == 1 || KG == 2, "K groups per workgroup");
   constexpr int kUpN = NU;                    // neurons per workgroup
   constexpr int kUpNB = kUpN / 16;            // MFMA neuron blocks
   constexpr int kUpLoads = kUpN * kUpPieces / 256;  // weight pieces per thread per stage
   using UpW = UpWn<kUpLoads>;
   constexpr int NBW = kUpNB * BB / 4;         // neuron blocks per wave
-  __shared__ __attribute__((aligned(16))) char wsm_[2 * kUpN * kUpRowB];
+  constexpr int kTileB = 2 * kUpN * kUpRowB;  // LDS bytes of one K group's weight tiles
+  __shared__ __attribute__((aligned(16))) char wsm_[KG * kTileB];
   const int nblocks = (a.n_pad + kUpN - 1) / kUpN;
   int t = blockIdx.x;
   const int nblk = t % nblocks;
@@ -343,13 +357,18 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
   const int n0 = nblk * kUpN;
   if (n0 >= n_sel) return;                    // whole workgroup: past the selection
   const int b0 = btile * 64;
-  const int kbeg = split * a.up_kper;
+  const int kg = KG == 1 ? 0 : static_cast<int>(threadIdx.x >> 8);  // K group of this wave
+  int kbeg = split * a.up_kper;
   const int kend = min(kbeg + a.up_kper, a.d);
-  const int nst = kend > kbeg ? (kend - kbeg) / kUpKc : 0;
+  int nst = kend > kbeg ? (kend - kbeg) / kUpKc : 0;
+  if (KG == 2) {
+    nst /= 2;                                 // even on the host's plans
+    kbeg += kg * nst * kUpKc;
+  }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, c = lane & 15;
-  lds_char_t* const wl = (lds_char_t*)(wsm_);
+  lds_char_t* const wl = (lds_char_t*)(wsm_) + kg * kTileB;
 
   // Weight pieces of this thread: piece index p = tid + 256 i -> row p >> 4
   // (= (tid >> 4) + 16 i), 16-byte column p & 15; 32-bit byte offsets of the
@@ -455,6 +474,57 @@ __global__ __launch_bounds__(256, 2) void sha_mlp_up_kernel(MlpArgs a) {
 
   // lane holds H^T[n = n0 + 16 mb + 4 q4 + r][b]: the computed rows of the
   // tile (16 BB of its 64).
+  if constexpr (KG == 2) {
+    // The second K group's sums go to its own LDS tiles (lane-linear 16-byte
+    // slots), the first group adds them, masks, applies ReLU and writes the
+    // 16-bit H tile to its LDS tiles, and all 512 threads copy whole rows out.
+    constexpr int kHPitch = kUpN * 2 + 16;    // bytes per staged H row
+    static_assert(4 * NBW * 64 * 16 <= kTileB && 16 * BB * kHPitch <= kTileB, "staging fits");
+    lds_char_t* const red = (lds_char_t*)(wsm_) + kTileB;
+    lds_char_t* const hl = (lds_char_t*)(wsm_);
+    __syncthreads();                          // the last stage's LDS reads are done
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < NBW; ++i)
+        *(lds_u32x4_t*)(red + ((wave * NBW + i) * 64 + lane) * 16) =
+            __builtin_bit_cast(u32x4_t, acc[i]);
+    }
+    __syncthreads();
+    if (kg == 0) {
+      const int row = 16 * (wu % BB) + c;
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const f32x4 v = __builtin_bit_cast(
+            f32x4, *(const lds_u32x4_t*)(red + ((wave * NBW + i) * 64 + lane) * 16));
+        const int nl = 16 * (grp * NBW + i) + 4 * q4;
+        float s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[r] = (0.f + acc[i][r]) + v[r];
+          if (!sel_valid(a, n0 + nl + r, n_sel)) s[r] = 0.f;
+        }
+        const uint32_t lo = M::pack(fmaxf(s[0], 0.f), fmaxf(s[1], 0.f));
+        const uint32_t hi = M::pack(fmaxf(s[2], 0.f), fmaxf(s[3], 0.f));
+        *(lds_u32x2_t*)(hl + row * kHPitch + nl * 2) = u32x2_t{lo, hi};
+      }
+    }
+    __syncthreads();
+    constexpr int kHPieces = kUpN / 8;        // 16-byte pieces per H row
+    char* const hbase = static_cast<char*>(a.h) + (static_cast<size_t>(b0) * a.n_pad + n0) * 2;
+#pragma unroll
+    for (int i = 0; i < (16 * BB * kHPieces + 511) / 512; ++i) {
+      const int idx = static_cast<int>(threadIdx.x) + 512 * i;
+      if (idx < 16 * BB * kHPieces) {
+        const int rr = idx / kHPieces, q = idx % kHPieces;
+        if (n0 + 8 * q < a.n_pad) {
+          const u32x4_t v = *(const lds_u32x4_t*)(hl + rr * kHPitch + q * 16);
+          *reinterpret_cast<uint4*>(hbase + (static_cast<size_t>(rr) * a.n_pad + 8 * q) * 2) =
+              __builtin_bit_cast(uint4, v);
+        }
+      }
+    }
+    return;
+  }
   if (a.up_splits > 1 && a.up_stage) {
     // fp32 K-split partials of a one-round grid leave in one burst: through
     // the weight tile in LDS as 16-byte pieces of whole rows (NU neurons of
@@ -954,8 +1024,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
 }
 
 // y = sum of the neuron-split partials, fixed order; one thread per 4
-// consecutive columns (d is a multiple of 256).  Loads of eight splits are
-// issued together, then summed in order.
+// consecutive columns (d is a multiple of 256).  Loads of sixteen splits are
+// issued together (the usual counts, up to 16, wait for memory once), then
+// summed in order.
 template <int DT>
 __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
   const size_t quads = static_cast<size_t>(a.B) * (a.d / 4);
@@ -963,13 +1034,13 @@ __global__ __launch_bounds__(256) void sha_mlp_down_finalize_kernel(MlpArgs a) {
   for (size_t i = blockIdx.x * 256 + threadIdx.x; i < quads; i += static_cast<size_t>(gridDim.x) * 256) {
     const float4* p = reinterpret_cast<const float4*>(a.dn_part) + i;  // row-major [b][d] of plane 0
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp0 = 0; sp0 < a.dn_splits; sp0 += 8) {
-      float4 v[8];
+    for (int sp0 = 0; sp0 < a.dn_splits; sp0 += 16) {
+      float4 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (sp0 + u < a.dn_splits) v[u] = p[(sp0 + u) * (plane / 4)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (sp0 + u < a.dn_splits) {
           s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
         }
@@ -991,11 +1062,17 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   if (BB <= 2 && a.up_xlds)
     hipLaunchKernelGGL((sha_mlp_upx_kernel<DT, BB <= 2 ? BB : 1>), dim3(static_cast<unsigned>(up_wgs)),
                        dim3(256), 0, st, a);
+  else if (BB == 4 && a.up_kg == 2 && a.up_nu == 144)
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, 4, 144, 2>), dim3(static_cast<unsigned>(up_wgs)),
+                       dim3(512), 0, st, a);
+  else if (BB == 4 && a.up_kg == 2)
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, 4, 128, 2>), dim3(static_cast<unsigned>(up_wgs)),
+                       dim3(512), 0, st, a);
   else if (BB == 4 && a.up_nu == 144)
-    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, 4, 144>), dim3(static_cast<unsigned>(up_wgs)),
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, 4, 144, 1>), dim3(static_cast<unsigned>(up_wgs)),
                        dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB, 128>), dim3(static_cast<unsigned>(up_wgs)),
+    hipLaunchKernelGGL((sha_mlp_up_kernel<DT, BB, 128, 1>), dim3(static_cast<unsigned>(up_wgs)),
                        dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

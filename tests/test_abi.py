@@ -177,12 +177,12 @@ def test_mlp_host_validation():
 def test_mlp_workspace_accounting():
     L = bd.lib()
     # OPT-66B MLP, all 36864 neurons selected, 64 rows, 256 CUs: H (64 x 36864
-    # 16-bit), the up projection's fp32 partials over 2 K splits (288
-    # workgroups of 128 neurons; 2 splits bring them to about one round of
-    # the 512 resident slots) and the down projection's over 14 neuron splits
-    # (36 column blocks x 14 ~ 2 workgroups per CU).
+    # 16-bit) and the down projection's fp32 partials over 14 neuron splits
+    # (18 column blocks of 512 x 14 ~ one workgroup per CU).  The up
+    # projection takes 256 workgroups of 144 neurons with two K groups each
+    # (one round at one per CU), so it has no K-split partials.
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 36864, 256)
-    assert ws == 64 * 36864 * 2 + 2 * 64 * 36864 * 4 + 14 * 64 * 9216 * 4
+    assert ws == 64 * 36864 * 2 + 14 * 64 * 9216 * 4
     # 21120 padded neurons (165 workgroups): 3 K splits (3072-element ranges)
     ws = L.sha_selective_mlp_workspace_bytes(8, 9216, 36864, 21033, 256)
     assert ws == 64 * 21120 * 2 + 3 * 64 * 21120 * 4 + 14 * 64 * 9216 * 4

@@ -134,13 +134,16 @@ def test_mixed_selective_mlp(i, monkeypatch):
     """Batches of 1-140 rows (every batch-block form, 1-3 batch tiles), with
     the planner's split counts and down workgroup form or forced ones
     (SHA_MLP_UP_SPLITS / SHA_MLP_DN_SPLITS / SHA_MLP_DN_WAVES /
-    SHA_MLP_UP_TILE, read by the library on every call)."""
+    SHA_MLP_UP_TILE / SHA_MLP_UP_KG, read by the library on every call)."""
     from oracle import mlp_union_ref, selective_mlp_ref
     w, pad = _mlp_case(i)
     us, ds = _mlp_splits(i)
     rw = np.random.default_rng(9700 + i)
     waves = int(rw.choice([0, 0, 4]))
     tile = int(rw.choice([0, 0, 128, 144]))
+    kg = int(np.random.default_rng(9800 + i).choice([0, 0, 1, 2]))
+    if kg:
+        monkeypatch.setenv("SHA_MLP_UP_KG", str(kg))
     if tile:
         monkeypatch.setenv("SHA_MLP_UP_TILE", str(tile))
     if waves:
@@ -151,7 +154,7 @@ def test_mixed_selective_mlp(i, monkeypatch):
         monkeypatch.setenv("SHA_MLP_DN_SPLITS", str(ds))
     say(f"[mixed mlp {i}] {w.dtype} B={w.B} d={w.d} D={w.D} k_row={w.k_row} pad={pad} "
         f"up_splits={us or 'plan'} dn_splits={ds or 'plan'} dn_waves={waves or 'plan'} "
-        f"up_tile={tile or 'plan'}")
+        f"up_tile={tile or 'plan'} up_kg={kg or 'plan'}")
     x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
     if pad and w.k_row > 0:                            # entries outside [0, D) are skipped
         rows = rows.clone()

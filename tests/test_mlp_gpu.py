@@ -143,6 +143,38 @@ def test_up_tiles_agree(B, d, D, k_row, monkeypatch):
     assert torch.equal(wl.raw_bits(outs[("2", "128")]), wl.raw_bits(outs[("2", "144")]))
 
 
+@pytest.mark.parametrize("B,d,D,k_row", [(64, 1024, 36864, 3686), (40, 512, 2000, 150),
+                                         (70, 256, 900, 60), (33, 768, 5000, 40),
+                                         (40, 256, 100, 30), (128, 1024, 4000, 300)])
+def test_up_k_groups_agree(B, d, D, k_row, monkeypatch):
+    """Full batch tiles: the 512-thread up workgroup that splits K between
+    its two halves and sums them on chip gives bit-identical outputs to two
+    K splits summed by the finalize (same halves, same order), for 128- and
+    144-neuron tiles, with one or two batch tiles and a single stage per
+    half (d = 256), and matches the oracle."""
+    say(f"[mlp] up K groups B={B} d={d} D={D} k_row={k_row}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 29 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    for tile in ("128", "144"):
+        outs = {}
+        monkeypatch.setenv("SHA_MLP_UP_TILE", tile)
+        for kg in ("1", "2"):
+            monkeypatch.setenv("SHA_MLP_UP_KG", kg)
+            if kg == "1":
+                monkeypatch.setenv("SHA_MLP_UP_SPLITS", "2")
+            else:
+                monkeypatch.delenv("SHA_MLP_UP_SPLITS", raising=False)
+            y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+            torch.cuda.synchronize()
+            err = float(np.abs(y.cpu().double().numpy() - ref).max())
+            assert err <= _tol("bf16", ref), (tile, kg, err)
+            outs[kg] = y.cpu()
+        assert torch.equal(wl.raw_bits(outs["1"]), wl.raw_bits(outs["2"])), tile
+
+
 @pytest.mark.parametrize("B,d,D,k_row,waves", [(64, 1024, 3000, 200, "8"), (64, 768, 3000, 200, "4"),
                                                (70, 512, 2000, 150, "8"), (16, 4096, 16384, 1638, "8"),
                                                (20, 1024, 1500, 60, "8"), (5, 768, 1000, 100, "4")])
