@@ -695,10 +695,12 @@ sha_status sha_mlp_union(const int32_t* row_neurons, int B, int k, int D, int32_
   if (!workspace || workspace_bytes < sha_mlp_union_workspace_bytes(D)) return SHA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SHA_ERR_MISALIGNED;
   (void)hipGetLastError();
-  // SHA_MLP_UNION_SMALL=0 (a tuning hook) keeps small unions on the three-kernel path.
+  // SHA_MLP_UNION_SMALL (a tuning hook): 0 keeps small unions on the
+  // three-kernel path, a value above 1 sets the one-workgroup bound (entries).
+  const int small = env_int("SHA_MLP_UNION_SMALL", 1);
   const hipError_t e = sha::launch_mlp_union(row_neurons, static_cast<int>(total), D, sel, n_sel,
                                              static_cast<uint8_t*>(workspace),
-                                             env_int("SHA_MLP_UNION_SMALL", 1) != 0, stream);
+                                             small == 1 ? -1 : (small < 0 ? 0 : small), stream);
   if (e != hipSuccess) {
     g_last_hip_error = e;
     return SHA_ERR_HIP;

@@ -47,10 +47,10 @@ struct MlpArgs {
 
 // flags: round_up(D, 256) bytes of workspace.
 int mlp_union_blocks(int D);
-// allow_small: at most 8192 entries and 2^18 neurons run as one workgroup
-// (flags unused).
+// small_max: unions of at most that many entries (and 2^18 neurons) run as
+// one workgroup (flags unused); -1 takes the library's bound, 0 never.
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, bool allow_small, hipStream_t stream);
+                            uint8_t* flags, int small_max, hipStream_t stream);
 hipError_t launch_selective_mlp(const MlpArgs& a, int dtype, hipStream_t stream);
 
 // Attention router: scores = x w^T (+ bias), per-row top-k heads.

@@ -1114,8 +1114,9 @@ hipError_t launch_mlp_t(const MlpArgs& a, hipStream_t st) {
 int mlp_union_blocks(int D) { return (D + kUnionBlockFlags - 1) / kUnionBlockFlags; }
 
 hipError_t launch_mlp_union(const int32_t* rows, int total, int D, int32_t* sel, int32_t* n_sel,
-                            uint8_t* flags, bool allow_small, hipStream_t st) {
-  if (allow_small && total <= kSmallUnionMaxTotal && D <= kSmallUnionMaxD) {
+                            uint8_t* flags, int small_max, hipStream_t st) {
+  const int lim = small_max < 0 ? kSmallUnionMaxTotal : small_max;
+  if (small_max != 0 && total <= lim && D <= kSmallUnionMaxD) {
     hipLaunchKernelGGL(sha_mlp_union_small_kernel, dim3(1), dim3(kSmallUnionThreads), 0, st, rows,
                        total, D, sel, n_sel);
     return hipGetLastError();
