@@ -447,7 +447,6 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   constexpr int NU = sha::kMlpUpNeurons;
   p.n_pad = ((n_max > 0 ? n_max : 1) + NU - 1) / NU * NU;
   p.b_pad = (B + 63) / 64 * 64;
-  p.bb = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
   const int kstages = d / sha::kMlpUpKc;
   // Up tile: 128 neurons, or for full batch tiles 144 when that leaves
   // fewer idle slots in the grid's last round of resident workgroups
@@ -462,19 +461,32 @@ MlpPlan mlp_plan(int B, int d, int n_max, int num_cus) {
   // finalize); the tile is then the one with fewer idle CUs in the last
   // round.  SHA_MLP_UP_KG = 1 or 2 forces one form (2 where d / 128 is even;
   // a tuning hook); SHA_MLP_UP_SPLITS keeps the four-wave form.
+  auto items_of = [&](int nu) {
+    return static_cast<long long>((p.n_pad + nu - 1) / nu) * (p.b_pad / 64);
+  };
+  auto kg2_fits = [&](int nu) {
+    const long long items = items_of(nu);
+    return items * 100 >= 95LL * cus && up_split_count(items, kstages, cus) >= 2;
+  };
+  const int kg_env = env_int("SHA_MLP_UP_KG", 0);
+  const bool kg2_allowed = kstages % 2 == 0 && env_int("SHA_MLP_UP_SPLITS", 0) <= 0 && kg_env != 1;
+  const bool kg2_fill = kg2_fits(NU) || kg2_fits(144);
+  // Batch blocks: 1 for B <= 16, 2 for B <= 32, else 4; batches of 17-32
+  // rows also compute the whole 64-row tile (padding rows repeat row B - 1,
+  // and no output row reads them) when the two-K-group form then fills the
+  // chip: the two-block grid of 128-neuron tiles runs past one round once
+  // the union passes ~33K neurons (OPT-66B B = 32, union + MLP in a graph:
+  // 244.4 -> 224.9 us; B = 24: 236.9 -> 216.3 us; B = 20 even).
+  // SHA_MLP_BB = 2 or 4 (a tuning hook) forces the blocks where B fits them.
+  p.bb = B <= 16 ? 1 : (B <= 32 && !(kg2_allowed && kg2_fill) ? 2 : 4);
+  {
+    const int bb = env_int("SHA_MLP_BB", 0);
+    if ((bb == 2 && B <= 32) || bb == 4) p.bb = bb;
+  }
   p.up_nu = NU;
   p.up_kg = 1;
   if (p.bb == 4) {
-    auto items_of = [&](int nu) {
-      return static_cast<long long>((p.n_pad + nu - 1) / nu) * (p.b_pad / 64);
-    };
-    auto kg2_fits = [&](int nu) {
-      const long long items = items_of(nu);
-      return items * 100 >= 95LL * cus && up_split_count(items, kstages, cus) >= 2;
-    };
-    const int kg_env = env_int("SHA_MLP_UP_KG", 0);
-    if (kstages % 2 == 0 && env_int("SHA_MLP_UP_SPLITS", 0) <= 0 && kg_env != 1 &&
-        (kg_env == 2 || kg2_fits(NU) || kg2_fits(144))) {
+    if (kg2_allowed && (kg_env == 2 || kg2_fill)) {
       p.up_kg = 2;
       auto idle = [&](int nu) {
         const long long items = items_of(nu);

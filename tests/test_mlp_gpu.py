@@ -175,6 +175,36 @@ def test_up_k_groups_agree(B, d, D, k_row, monkeypatch):
         assert torch.equal(wl.raw_bits(outs["1"]), wl.raw_bits(outs["2"])), tile
 
 
+@pytest.mark.parametrize("B,d,D,k_row", [(32, 1024, 36864, 3686), (24, 512, 36864, 3000),
+                                         (20, 256, 36864, 2000), (17, 768, 40000, 3000),
+                                         (30, 512, 3000, 200)])
+def test_full_tiles_for_two_blocks_agree(B, d, D, k_row, monkeypatch):
+    """Batches of 17-32 rows computed as two batch blocks or as the whole
+    64-row tile (the plan's choice when the two-K-group up form then fills
+    the chip; padding rows repeat row B - 1 and are never stored) give
+    bit-identical outputs (per neuron and output the same K stages, splits
+    and chunks in the same order) and match the oracle."""
+    say(f"[mlp] full tiles for two blocks B={B} d={d} D={D} k_row={k_row}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="bf16", seed=B * 31 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    outs = {}
+    for bb in ("2", "4", None):
+        if bb:
+            monkeypatch.setenv("SHA_MLP_BB", bb)
+        else:
+            monkeypatch.delenv("SHA_MLP_BB", raising=False)
+        y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+        torch.cuda.synchronize()
+        err = float(np.abs(y.cpu().double().numpy() - ref).max())
+        assert err <= _tol("bf16", ref), (bb, err)
+        outs[bb] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs["2"]), wl.raw_bits(outs["4"]))
+    assert torch.equal(wl.raw_bits(outs["2"]), wl.raw_bits(outs[None]))
+
+
 @pytest.mark.parametrize("B,d,D,k_row,waves", [(64, 1024, 3000, 200, "8"), (64, 768, 3000, 200, "4"),
                                                (70, 512, 2000, 150, "8"), (16, 4096, 16384, 1638, "8"),
                                                (20, 1024, 1500, 60, "8"), (5, 768, 1000, 100, "4")])
