@@ -784,6 +784,11 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
   // 126.8 us at OPT-66B B = 64); SHA_MLP_DN_STAGE=0 (a tuning hook) keeps
   // the direct 4-byte stores.
   a.dn_stage = env_int("SHA_MLP_DN_STAGE", 1) != 0;
+  // One or two batch blocks with 2-4 up K splits: the down projection sums
+  // the up partials as it loads H (no up finalize launch; OPT-6.7B B = 16 and
+  // OPT-66B B = 8); SHA_MLP_FUSE_UP=0 (a tuning hook) keeps the finalize.
+  a.dn_fuse_up = p.bb <= 2 && p.up_splits >= 2 && p.up_splits <= 4 &&
+                 env_int("SHA_MLP_FUSE_UP", 1) != 0;
   (void)hipGetLastError();
   const hipError_t e = sha::launch_selective_mlp(a, dtype, stream);
   if (e != hipSuccess) {

@@ -43,6 +43,8 @@ struct MlpArgs {
   int dn_stage;         // down split partials stored through LDS as whole-row pieces
   int dn_waves;         // waves per down workgroup (64 output columns each): 4, or 8
                         // when d is a multiple of 512
+  int dn_fuse_up;       // bb <= 2 with 2-4 up K splits: the down projection sums the
+                        // up partials itself (no up finalize; H unused)
 };
 
 // flags: round_up(D, 256) bytes of workspace.

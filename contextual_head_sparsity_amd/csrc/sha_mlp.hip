@@ -33,7 +33,9 @@
 //            gathered W2t rows are staged in LDS and read back transposed
 //            (ds_read_b64_tr_b16) as B operands, H comes from LDS as A.
 //            Split ranges of neurons write fp32 partials that
-//            `down_finalize` sums in a fixed order.
+//            `down_finalize` sums in a fixed order.  For one or two batch
+//            blocks with 2-4 up K splits it sums the up partials itself as
+//            it loads H (the up finalize's arithmetic; no finalize launch).
 //   Batches of at most 16 (32) rows compute only the 1 (2) batch blocks of
 //   16 rows that hold rows: in the up projection the waves then split the
 //   tile's neurons instead of its batch blocks, and the waves sharing a
@@ -801,16 +803,35 @@ constexpr int kDnHPitch = kDnKc * 2 + 16;   // 144 B: conflict-free H reads
 // reads).  The register budget is 256 per lane either way, accumulators
 // included.  BB = 16-row batch blocks computed per 64-row tile (as in the up
 // projection): only those rows of H are multiplied.
-template <int DT, int BB, int NW>
+//
+// FU (one or two batch blocks, 2-4 up K splits): the up finalize is folded
+// in.  Instead of H, a workgroup loads each chunk's fp32 up partials (every
+// split, unconditionally, the split index clamped), sums them in split
+// order from zero, applies ReLU and rounds to 16 bits as it writes the
+// chunk's H rows to LDS: exactly the finalize's arithmetic, so H and y are
+// bit-identical, and the finalize launch is gone.
+constexpr int kFuSplits = 4;                // up K splits the folded form reads (at most)
+template <int DT, int BB, int NW, bool FU>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a) {
   using M = Mx<DT>;
   static_assert(BB == 1 || BB == 2 || BB == 4, "batch blocks per tile");
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(!FU || BB <= 2, "the folded up finalize: one or two batch blocks");
   constexpr int T = 64 * NW;                  // threads
   constexpr int kDnCols = 64 * NW;            // output columns per workgroup
   constexpr int kDnWPitch = kDnCols * 2 + 32; // 544 / 1056 B: conflict-free transposed reads
   constexpr int RP = kDnCols / 8;             // 16-byte pieces per weight row
   constexpr int HL = (BB == 4 ? 512 : 256) / T > 0 ? (BB == 4 ? 512 : 256) / T : 1;  // H pieces per thread
+  // Folded finalize: each thread sums kFuE consecutive neurons of one H row.
+  constexpr int kFuE = 16 * BB * kDnKc / T;
+  static_assert(!FU || kFuE == 2 || kFuE == 4 || kFuE == 8, "neurons per thread");
+  struct HSet {
+    uint4 v[HL];
+  };
+  struct PSet {
+    float v[kFuSplits * (kFuE > 0 ? kFuE : 1)];
+  };
+  using HR = std::conditional_t<FU, PSet, HSet>;
   __shared__ __attribute__((aligned(16))) char ws_[kDnKc * kDnWPitch];
   __shared__ __attribute__((aligned(16))) char hs_[64 * kDnHPitch];
   const int n_sel = sel_count(a);
@@ -858,7 +879,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
   // for them, and (loads complete in order) for every older load, at once.
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const bool upper = lane >= 32;
-  auto load_chunk = [&](int k0, uint4 (&wv)[8], uint4 (&hv)[HL]) {
+  auto load_chunk = [&](int k0, uint4 (&wv)[8], HR& hv) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int row;
@@ -874,13 +895,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
       wv[i] = ld16_stream(static_cast<const char*>(a.w2t) +
                           (static_cast<size_t>(row) * a.d + col0 + (lane % RP) * 8) * 2);
     }
+    if constexpr (FU) {
+      // Partials of neurons nc .. nc + kFuE - 1 of row r, every split (a
+      // split past up_splits reads the last one again and is not summed).
+      const int r = tid / (kDnKc / kFuE), ng = tid % (kDnKc / kFuE);
+      const int nc = min(k0 + ng * kFuE, a.n_pad - kFuE);  // past n_pad: past nend, masked
 #pragma unroll
-    for (int i = 0; i < HL; ++i) {
-      const int idx = tid + T * i;
-      const int r = idx >> 3, piece = idx & 7;
-      const int nc = min(k0 + piece * 8, a.n_pad - 8);  // past n_pad: past nend, masked
-      hv[i] = ld16(static_cast<const char*>(a.h) +
-                   (static_cast<size_t>(b0 + r) * a.n_pad + nc) * 2);
+      for (int sp = 0; sp < kFuSplits; ++sp) {
+        const int sv = min(sp, a.up_splits - 1);
+        const float* src =
+            a.up_part + (static_cast<size_t>(sv) * a.b_pad + b0 + r) * a.n_pad + nc;
+        if constexpr (kFuE == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(src);
+          hv.v[sp * kFuE] = t.x;
+          hv.v[sp * kFuE + 1] = t.y;
+        } else {
+#pragma unroll
+          for (int q = 0; q < kFuE / 4; ++q) {
+            const float4 t = *reinterpret_cast<const float4*>(src + 4 * q);
+            hv.v[sp * kFuE + 4 * q] = t.x;
+            hv.v[sp * kFuE + 4 * q + 1] = t.y;
+            hv.v[sp * kFuE + 4 * q + 2] = t.z;
+            hv.v[sp * kFuE + 4 * q + 3] = t.w;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < HL; ++i) {
+        const int idx = tid + T * i;
+        const int r = idx >> 3, piece = idx & 7;
+        const int nc = min(k0 + piece * 8, a.n_pad - 8);  // past n_pad: past nend, masked
+        hv.v[i] = ld16(static_cast<const char*>(a.h) +
+                       (static_cast<size_t>(b0 + r) * a.n_pad + nc) * 2);
+      }
     }
   };
 
@@ -889,7 +937,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
   // set with chunk j + 2 (two chunks in flight during the products), publish
   // and multiply.  CHECK: only load inside the range.
   const int nch = nend > nbeg ? (nend - nbeg + kDnKc - 1) / kDnKc : 0;
-  auto step = [&](int j, uint4 (&w)[8], uint4 (&h)[HL], auto check) {
+  auto step = [&](int j, uint4 (&w)[8], HR& h, auto check) {
     constexpr bool C = decltype(check)::value;
     __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
@@ -898,17 +946,48 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
       const int r = idx / RP, piece = idx % RP;
       *(lds_u32x4_t*)(wl + r * kDnWPitch + piece * 16) = __builtin_bit_cast(u32x4_t, w[i]);
     }
+    if constexpr (FU) {
+      // The finalize's sum (from zero, in split order), ReLU and rounding;
+      // neurons at or past nend are zero.
+      const int r = tid / (kDnKc / kFuE), ng = tid % (kDnKc / kFuE);
+      const int kk0 = nbeg + j * kDnKc + ng * kFuE;
+      float sum[kFuE];
 #pragma unroll
-    for (int i = 0; i < HL; ++i) {
-      const int idx = tid + T * i;
-      const int r = idx >> 3, piece = idx & 7;
-      const int cnt = min(max(nend - (nbeg + j * kDnKc + piece * 8), 0), 8);  // valid neurons
-      uint32_t m[4];
+      for (int e = 0; e < kFuE; ++e) sum[e] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        m[e] = (2 * e < cnt ? 0x0000FFFFu : 0u) | (2 * e + 1 < cnt ? 0xFFFF0000u : 0u);
-      const u32x4_t hm = {h[i].x & m[0], h[i].y & m[1], h[i].z & m[2], h[i].w & m[3]};
-      *(lds_u32x4_t*)(hl + r * kDnHPitch + piece * 16) = hm;
+      for (int sp = 0; sp < kFuSplits; ++sp)
+        if (sp < a.up_splits) {
+#pragma unroll
+          for (int e = 0; e < kFuE; ++e) sum[e] += h.v[sp * kFuE + e];
+        }
+      uint32_t pk[kFuE / 2];
+#pragma unroll
+      for (int e = 0; e < kFuE / 2; ++e) {
+        const float lo = kk0 + 2 * e < nend ? fmaxf(sum[2 * e], 0.f) : 0.f;
+        const float hi = kk0 + 2 * e + 1 < nend ? fmaxf(sum[2 * e + 1], 0.f) : 0.f;
+        pk[e] = M::pack(lo, hi);
+      }
+      lds_char_t* const dst = hl + r * kDnHPitch + ng * kFuE * 2;
+      if constexpr (kFuE == 2) {
+        *(lds_u32_t*)(dst) = pk[0];
+      } else if constexpr (kFuE == 4) {
+        *(lds_u32x2_t*)(dst) = u32x2_t{pk[0], pk[1]};
+      } else {
+        *(lds_u32x4_t*)(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < HL; ++i) {
+        const int idx = tid + T * i;
+        const int r = idx >> 3, piece = idx & 7;
+        const int cnt = min(max(nend - (nbeg + j * kDnKc + piece * 8), 0), 8);  // valid neurons
+        uint32_t m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          m[e] = (2 * e < cnt ? 0x0000FFFFu : 0u) | (2 * e + 1 < cnt ? 0xFFFF0000u : 0u);
+        const u32x4_t hm = {h.v[i].x & m[0], h.v[i].y & m[1], h.v[i].z & m[2], h.v[i].w & m[3]};
+        *(lds_u32x4_t*)(hl + r * kDnHPitch + piece * 16) = hm;
+      }
     }
     if (!C || j + 2 < nch) load_chunk(nbeg + (j + 2) * kDnKc, w, h);
     // Keep the loads ahead of the products: the scheduler would otherwise
@@ -946,7 +1025,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void sha_mlp_down_kernel(MlpArgs a
     // at the loop head from the entry and from the back edge and can leave
     // the younger set in flight; a conditional second load makes it wait
     // for everything there.
-    uint4 wa[8], ha0[HL], wb8[8], hb0[HL];
+    uint4 wa[8], wb8[8];
+    HR ha0, hb0;
     load_chunk(nbeg, wa, ha0);
     load_chunk(nbeg + min(1, nch - 1) * kDnKc, wb8, hb0);
     using Chk = std::true_type;
@@ -1059,6 +1139,9 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   const unsigned btiles = static_cast<unsigned>(a.b_pad / 64);
   const long long up_wgs =
       static_cast<long long>((a.n_pad + a.up_nu - 1) / a.up_nu) * a.up_splits * btiles;
+  // The two-K-group form writes H itself: one K split, two equal halves.
+  if (a.up_kg == 2 && (BB != 4 || a.up_splits != 1 || (a.d / kMlpUpKc) % 2 != 0))
+    return hipErrorInvalidValue;
   if (BB <= 2 && a.up_xlds)
     hipLaunchKernelGGL((sha_mlp_upx_kernel<DT, BB <= 2 ? BB : 1>), dim3(static_cast<unsigned>(up_wgs)),
                        dim3(256), 0, st, a);
@@ -1076,7 +1159,10 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
                        dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.up_splits > 1) {
+  // With the finalize folded into the down projection, H is never written.
+  const bool fold = BB <= 2 && a.dn_fuse_up;
+  if (fold && (a.up_splits < 2 || a.up_splits > kFuSplits)) return hipErrorInvalidValue;
+  if (a.up_splits > 1 && !fold) {
     const size_t quads = static_cast<size_t>(btiles) * 16 * BB * (a.n_pad / 4);
     const unsigned blocks = static_cast<unsigned>(quads < 256 * 1024 ? (quads + 255) / 256 : 1024);
     hipLaunchKernelGGL((sha_mlp_up_finalize_kernel<DT>), dim3(blocks), dim3(256), 0, st, a);
@@ -1085,10 +1171,15 @@ hipError_t launch_mlp_bb(const MlpArgs& a, hipStream_t st) {
   // 1-D over (column block, split, batch tile): the kernel maps the ids
   // onto XCDs itself.
   const dim3 dn_grid(static_cast<unsigned>((a.d / dn_cols) * a.dn_splits) * btiles);
-  if (a.dn_waves == 8)
-    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 8>), dn_grid, dim3(512), 0, st, a);
+  constexpr int BF = BB <= 2 ? BB : 1;       // batch blocks of the folded form
+  if (fold && a.dn_waves == 8)
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BF, 8, true>), dn_grid, dim3(512), 0, st, a);
+  else if (fold)
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BF, 4, true>), dn_grid, dim3(256), 0, st, a);
+  else if (a.dn_waves == 8)
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 8, false>), dn_grid, dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 4>), dn_grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((sha_mlp_down_kernel<DT, BB, 4, false>), dn_grid, dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.dn_splits > 1) {
     const size_t total = static_cast<size_t>(a.B) * (a.d / 4);

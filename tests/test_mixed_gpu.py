@@ -134,8 +134,8 @@ def test_mixed_selective_mlp(i, monkeypatch):
     """Batches of 1-140 rows (every batch-block form, 1-3 batch tiles), with
     the planner's split counts and down workgroup form or forced ones
     (SHA_MLP_UP_SPLITS / SHA_MLP_DN_SPLITS / SHA_MLP_DN_WAVES /
-    SHA_MLP_UP_TILE / SHA_MLP_UP_KG / SHA_MLP_BB, read by the library on
-    every call)."""
+    SHA_MLP_UP_TILE / SHA_MLP_UP_KG / SHA_MLP_BB / SHA_MLP_FUSE_UP, read by
+    the library on every call)."""
     from oracle import mlp_union_ref, selective_mlp_ref
     w, pad = _mlp_case(i)
     us, ds = _mlp_splits(i)
@@ -148,6 +148,8 @@ def test_mixed_selective_mlp(i, monkeypatch):
     bb = int(np.random.default_rng(10000 + i).choice([0, 0, 0, 2, 4]))
     if bb:
         monkeypatch.setenv("SHA_MLP_BB", str(bb))
+    fold = int(np.random.default_rng(10100 + i).choice([1, 1, 0]))
+    monkeypatch.setenv("SHA_MLP_FUSE_UP", str(fold))
     if tile:
         monkeypatch.setenv("SHA_MLP_UP_TILE", str(tile))
     if waves:
@@ -158,7 +160,7 @@ def test_mixed_selective_mlp(i, monkeypatch):
         monkeypatch.setenv("SHA_MLP_DN_SPLITS", str(ds))
     say(f"[mixed mlp {i}] {w.dtype} B={w.B} d={w.d} D={w.D} k_row={w.k_row} pad={pad} "
         f"up_splits={us or 'plan'} dn_splits={ds or 'plan'} dn_waves={waves or 'plan'} "
-        f"up_tile={tile or 'plan'} up_kg={kg or 'plan'} bb={bb or 'plan'}")
+        f"up_tile={tile or 'plan'} up_kg={kg or 'plan'} bb={bb or 'plan'} fold={fold}")
     x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
     if pad and w.k_row > 0:                            # entries outside [0, D) are skipped
         rows = rows.clone()

@@ -175,6 +175,35 @@ def test_up_k_groups_agree(B, d, D, k_row, monkeypatch):
         assert torch.equal(wl.raw_bits(outs["1"]), wl.raw_bits(outs["2"])), tile
 
 
+@pytest.mark.parametrize("B,d,D,k_row,splits", [(16, 4096, 16384, 1638, None),
+                                                (8, 9216, 36864, 3686, None),
+                                                (20, 1024, 3000, 200, "2"), (5, 768, 1000, 100, "3"),
+                                                (30, 768, 5000, 300, "4"), (1, 512, 700, 650, "4"),
+                                                (12, 256, 2000, 150, "2")])
+def test_down_folds_up_finalize_agree(B, d, D, k_row, splits, monkeypatch):
+    """One or two batch blocks with 2-4 up K splits: the down projection
+    summing the up partials itself gives bit-identical outputs to the up
+    finalize followed by the down projection (4- and 8-wave down
+    workgroups, selections ending inside a chunk) and matches the oracle."""
+    say(f"[mlp] folded up finalize B={B} d={d} D={D} k_row={k_row} splits={splits}")
+    w = wl.MlpWorkload("t", B=B, d=d, D=D, k_row=k_row, dtype="f16", seed=B * 37 + d)
+    x, w1t, w2t, rows = wl.make_mlp(w, "cpu")
+    sel, n_sel = sha.mlp_union(rows.to(DEV), D)
+    ref = selective_mlp_ref(x, w1t, w2t, mlp_union_ref(rows, D))
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    if splits:
+        monkeypatch.setenv("SHA_MLP_UP_SPLITS", splits)
+    outs = {}
+    for fold in ("0", "1"):
+        monkeypatch.setenv("SHA_MLP_FUSE_UP", fold)
+        y = sha.selective_mlp(xd, w1d, w2d, sel, n_sel, n_max=sel.numel())
+        torch.cuda.synchronize()
+        err = float(np.abs(y.cpu().double().numpy() - ref).max())
+        assert err <= _tol("f16", ref), (fold, err)
+        outs[fold] = y.cpu()
+    assert torch.equal(wl.raw_bits(outs["0"]), wl.raw_bits(outs["1"]))
+
+
 @pytest.mark.parametrize("B,d,D,k_row", [(32, 1024, 36864, 3686), (24, 512, 36864, 3000),
                                          (20, 256, 36864, 2000), (17, 768, 40000, 3000),
                                          (30, 512, 3000, 200)])
