@@ -351,6 +351,28 @@ def test_selection_edge_cases(dtype):
     assert float(np.abs(got - ref).max()) <= _tol(dtype, ref)
 
 
+@pytest.mark.parametrize("B,D", [(64, 36864), (24, 36864), (8, 36864), (40, 600)])
+def test_selection_edge_cases_every_plan(B, D):
+    """The edge cases above under each planned form: n_max = D = 36864 at
+    B = 64 and 24 takes 256 up workgroups with two K groups (B = 24 as a
+    whole 64-row tile), B = 8 the folded up finalize; B = 40 with a small D
+    the four-wave form with K splits.  An empty selection gives zeros and
+    padding entries inside a short count contribute nothing."""
+    say(f"[mlp] edge cases under the plan for B={B} D={D}")
+    w = wl.MlpWorkload("t", B=B, d=256, D=D, k_row=10, dtype="bf16", seed=B + 11)
+    x, w1t, w2t, _ = wl.make_mlp(w, "cpu")
+    xd, w1d, w2d = x.to(DEV), w1t.to(DEV), w2t.to(DEV)
+    sel = torch.zeros(D, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    assert np.array_equal(_run(xd, w1d, w2d, sel, cnt, n_max=D), np.zeros((B, 256)))
+    entries = np.array([D - 1, -1, 3, D + 5, 250, 7, 42, D - 1, 599], dtype=np.int32)
+    sel = torch.from_numpy(np.concatenate([entries, np.full(D - len(entries), 5, np.int32)])).to(DEV)
+    cnt = torch.tensor([len(entries)], dtype=torch.int32, device=DEV)
+    got = _run(xd, w1d, w2d, sel, cnt, n_max=D)
+    ref = selective_mlp_ref(x, w1t, w2t, entries)
+    assert float(np.abs(got - ref).max()) <= _tol("bf16", ref)
+
+
 def test_dense_selection_and_determinism():
     say("[mlp] dense + determinism")
     w = wl.MlpWorkload("t", B=64, d=512, D=3000, k_row=3000, dtype="bf16", seed=3)
