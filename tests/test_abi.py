@@ -190,6 +190,15 @@ def test_mlp_workspace_accounting():
     # projection's K 8 ways (1152-element ranges) and keeps a single down split
     ws = L.sha_selective_mlp_workspace_bytes(64, 9216, 36864, 64, 256)
     assert ws == 64 * 128 * 2 + 8 * 64 * 128 * 4
+    # 24 rows of the OPT-66B MLP: the whole 64-row tile with two K groups
+    # (no up partials), as at 64 rows
+    ws = L.sha_selective_mlp_workspace_bytes(24, 9216, 36864, 36864, 256)
+    assert ws == 64 * 36864 * 2 + 14 * 64 * 9216 * 4
+    # 32 rows of the OPT-6.7B MLP: 128 tiles cannot fill the chip at one
+    # workgroup per CU, so two batch blocks with 4 up K splits (and the
+    # down projection's 8 column blocks x 32 neuron splits)
+    ws = L.sha_selective_mlp_workspace_bytes(32, 4096, 16384, 16384, 256)
+    assert ws == 64 * 16384 * 2 + 4 * 64 * 16384 * 4 + 32 * 64 * 4096 * 4
 
 
 def test_router_host_validation():
