@@ -115,6 +115,9 @@ def parse():
                    help="MLP shape inside the decode step (its dtype follows the workload)")
     p.add_argument("--router", default=None, choices=list(wl.WORKLOADS),
                    help="time the attention router (scores + per-row top-k) of this layer shape")
+    p.add_argument("--router-onepass", action="store_true",
+                   help="with --router: time the one-pass kernels (no workspace) even where "
+                        "the library picks the K-split form")
     p.add_argument("--router-floor", action="store_true",
                    help="with --router: also time the same graph of calls on tiny inputs")
     return p.parse_args()
@@ -631,12 +634,16 @@ def bench_router(args):
     idx = torch.empty(w.B, w.top_k, dtype=torch.int32, device=dev)
     sc = torch.empty(w.B, nh, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    split = False if getattr(args, "router_onepass", False) else None
+    need = sha.router_workspace_bytes(w.B, dm, nh, dt, split)
+    rws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    kw = dict(bias=bias, index=idx, scores=sc, workspace=rws, split=split)
 
     def cold(i):
-        sha.router_topk(x, ws[i % copies], w.top_k, bias=bias, index=idx, scores=sc, stream=stream)
+        sha.router_topk(x, ws[i % copies], w.top_k, stream=stream, **kw)
 
     def warm(i):
-        sha.router_topk(x, w0, w.top_k, bias=bias, index=idx, scores=sc, stream=stream)
+        sha.router_topk(x, w0, w.top_k, stream=stream, **kw)
 
     def graph_us(call, n):
         return graph_us_per_call(call, n, dev, max(args.warmup // 50, 2), max(args.steps // 50, 3))
@@ -644,8 +651,8 @@ def bench_router(args):
     def captured(weights_of):
         # calls on the current (capturing) stream
         def call(i):
-            sha.router_topk(x, weights_of(i), w.top_k, bias=bias, index=idx, scores=sc,
-                            stream=torch.cuda.current_stream(dev))
+            sha.router_topk(x, weights_of(i), w.top_k, stream=torch.cuda.current_stream(dev),
+                            **kw)
         return call
 
     g_cold = graph_us(captured(lambda i: ws[i % copies]), copies)
@@ -658,8 +665,12 @@ def bench_router(args):
         it = torch.empty(B, k, dtype=torch.int32, device=dev) if k else None
         st = torch.empty(B, nh_, dtype=torch.float32, device=dev)
 
+        tws = torch.empty(max(sha.router_workspace_bytes(B, dm_, nh_, dt, split), 1),
+                          dtype=torch.uint8, device=dev)
+
         def call(i):
-            sha.router_topk(xt, wt, k, index=it, scores=st, stream=torch.cuda.current_stream(dev))
+            sha.router_topk(xt, wt, k, index=it, scores=st, stream=torch.cuda.current_stream(dev),
+                            workspace=tws, split=split)
         return round(graph_us(call, 2000), 2)
 
     floor = None
@@ -678,7 +689,8 @@ def bench_router(args):
            "data": "synthetic: seeded N(0,1) hidden states, N(0, 1/d_model) router weights, "
                    "N(0,1) bias",
            "config": {"workload": w.name, "B": w.B, "d_model": dm, "heads": nh, "top_k": w.top_k,
-                      "gqa": w.gqa, "weight_bytes": wbytes, "weight_copies_rotated": copies},
+                      "gqa": w.gqa, "weight_bytes": wbytes, "weight_copies_rotated": copies,
+                      "form": "k-split" if need > 0 else "one-pass"},
            "roofline": {"bound": "latency", "achieved": round(nbytes / (g_cold / 1e6) / 1e9, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(nbytes / (g_cold / 1e6) / 1e9 / HBM_PEAK_GBS, 4),

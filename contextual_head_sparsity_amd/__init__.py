@@ -9,7 +9,8 @@ from . import workloads
 
 _BINDING_NAMES = ("sha_decode", "sha_decode_gqa", "sha_decode_paged", "KvLayout", "DecodeStep",
                   "ShaError", "lib", "plan_nsplit", "workspace_bytes", "workspace_bytes_paged",
-                  "router_topk", "mlp_union", "selective_mlp", "selective_mlp_workspace_bytes")
+                  "router_topk", "router_workspace_bytes", "mlp_union", "selective_mlp",
+                  "selective_mlp_workspace_bytes")
 
 __all__ = ["workloads", *_BINDING_NAMES]
 

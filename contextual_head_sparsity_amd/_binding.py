@@ -80,6 +80,9 @@ SIGNATURES = {
     "sha_selective_mlp_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "sha_selective_mlp": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _S]),
     "sha_router_topk": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I]),
+    "sha_router_split_bytes": (_S, [_I, _I, _I, _I]),
+    "sha_router_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "sha_router_topk_ex": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _S]),
     "sha_step_create": (_I, [ctypes.POINTER(StepConfig), ctypes.POINTER(StepLayer), _I, _I,
                              ctypes.POINTER(ctypes.c_void_p)]),
     "sha_step_run": (_I, [_P, _P]),
@@ -385,11 +388,24 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
 # attention router
 # ---------------------------------------------------------------------------
 
-def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
+def router_workspace_bytes(B, d, H, dtype, split=None) -> int:
+    """Workspace bytes of the router's K-split form: where the library picks
+    it (split=None), for any shape that has it (True), or 0 (False)."""
+    if split is False:
+        return 0
+    fn = lib().sha_router_split_bytes if split else lib().sha_router_workspace_bytes
+    return fn(B, d, H, _DT[dtype])
+
+
+def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None, workspace=None,
+                split=None):
     """Attention router on the device: scores = x w^T (+ bias), the top_k heads
     per row in ascending order.  x [B, d], w [H, d] (f32 / f16 / bf16), bias
     [H] fp32.  Returns (index [B, top_k] int32, scores [B, H] fp32).  Runs on
-    `stream` (default: the current stream)."""
+    `stream` (default: the current stream).  split=None takes the K-split
+    form where the library finds it faster, True wherever the shape has one,
+    False never; it runs in `workspace` (a device byte tensor) or a
+    temporary one."""
     for name, t in (("x", x), ("w", w)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
             raise ValueError(f"{name} must be a contiguous 2-D device tensor")
@@ -415,12 +431,16 @@ def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None):
         elif scores.dtype != torch.float32 or not scores.is_contiguous() or \
                 tuple(scores.shape) != (B, H):
             raise ValueError("scores must be a contiguous float32 [B, H] tensor")
+        need = router_workspace_bytes(B, d, H, x.dtype, split)
+        if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
         with torch.cuda.device(x.device):
-            st = lib().sha_router_topk(x.data_ptr(), w.data_ptr(),
-                                       bias.data_ptr() if bias is not None else None, B, d, H,
-                                       top_k, index.data_ptr(), scores.data_ptr(),
-                                       stream.cuda_stream, _DT[x.dtype])
-    _check(st, "sha_router_topk")
+            st = lib().sha_router_topk_ex(x.data_ptr(), w.data_ptr(),
+                                          bias.data_ptr() if bias is not None else None, B, d, H,
+                                          top_k, index.data_ptr(), scores.data_ptr(),
+                                          stream.cuda_stream, _DT[x.dtype],
+                                          workspace.data_ptr() if need > 0 else None, need)
+    _check(st, "sha_router_topk_ex")
     return index, scores
 
 

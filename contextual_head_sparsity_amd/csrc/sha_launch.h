@@ -64,7 +64,16 @@ struct RouterArgs {
   float* scores;        // [B, H] fp32 (output)
   int32_t* index;       // [B, top_k] (output, ascending head ids)
   int B, d, H, top_k;
+  float* part;          // [B, nchunk, H] fp32 K-split partials, or null (one-pass form)
+  int nchunk;           // hidden-dimension chunks of kRouterChunk elements
 };
+
+// K-split router form: 16-bit inputs, at most kRouterSplitMaxH heads and
+// kRouterSplitMaxB rows; one partial per (row, chunk of kRouterChunk hidden
+// elements, head).
+constexpr int kRouterChunk = 256;
+constexpr int kRouterSplitMaxH = 128;
+constexpr int kRouterSplitMaxB = 4096;
 
 // num_cus: the device's compute units (picks the heads per scores workgroup).
 hipError_t launch_router(const RouterArgs& a, int dtype, int num_cus, hipStream_t stream);

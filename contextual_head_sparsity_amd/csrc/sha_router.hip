@@ -15,6 +15,21 @@
 //                  pieces (v_dot2 for 16-bit inputs, fp32 accumulation), DPP
 //                  + shuffle wave sums, the waves' partials added in a fixed
 //                  order.
+//   K-split form (16-bit inputs, H <= 128, B <= 4096, a caller workspace):
+//                  a workgroup of four waves owns 16 batch rows and 256
+//                  hidden elements (64 per wave in two 32-element
+//                  v_mfma_f32_16x16x32 steps: A = 16 rows of x, B = 16 heads
+//                  of w, every head block of the layer), the waves' products
+//                  added in LDS in wave order and stored as one fp32 partial
+//                  per (row, 256-element chunk, head); the top-k workgroup of
+//                  a row adds its partials in chunk order, adds the bias and
+//                  writes the scores before ranking them.  Each workgroup
+//                  reads 16 rows x 256 elements of x once and the same 256
+//                  columns of w, so the whole call reads x once and w once per
+//                  16 rows (from L2 after the first).  Many short workgroups
+//                  instead of a long dot product per (row, heads) pay where
+//                  the call has many multiply-adds (B H d >= 2^24); below
+//                  that the one-pass kernels are faster.
 //   top-k kernel : one workgroup of four waves per batch row; each head's
 //                  rank in the (score descending, index ascending) order
 //                  (NaN ranked as -inf) is a count of larger 64-bit keys
@@ -107,6 +122,91 @@ __global__ __launch_bounds__(kScoreWaves * 64) void sha_router_scores_kernel(Rou
   }
 }
 
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 rf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x4 __attribute__((ext_vector_type(4)));
+
+// 16 x 16 x 32 matrix-core product with fp32 accumulation.  Operand layout
+// (lane l, q = l / 16, c = l % 16): A[i][k] holds i = c, k = 8q .. 8q+7;
+// B[k][j] holds j = c, k = 8q .. 8q+7; the result D[i][j] holds
+// i = 4q .. 4q+3, j = c.
+template <int DT>
+__device__ __forceinline__ rf32x4 mma16(uint4 a, uint4 b, rf32x4 c);
+template <>
+__device__ __forceinline__ rf32x4 mma16<kF16>(uint4 a, uint4 b, rf32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(rf16x8_t, a),
+                                                __builtin_bit_cast(rf16x8_t, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ rf32x4 mma16<kBF16>(uint4 a, uint4 b, rf32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rbf16x8_t, a),
+                                                 __builtin_bit_cast(rbf16x8_t, b), c, 0, 0, 0);
+}
+
+constexpr int kPartWaves = 4;                          // waves per partial workgroup
+constexpr int kPartRows = 16;                          // batch rows per workgroup
+
+// Workgroup (row block rb, chunk ch) of the K-split form, NHB = ceil(H / 16)
+// head blocks.  Wave w covers hidden elements [ch*256 + w*64, +64); every
+// load of the wave is issued before the first product.  Rows past B read
+// row B - 1 and heads past H read head H - 1 (never stored); hidden
+// elements past d (a ragged last chunk; d is a multiple of 8, so a lane's
+// 8 elements are all in or all out) are zeroed in both operands.
+template <int DT, int NHB>
+__global__ __launch_bounds__(kPartWaves * 64) void sha_router_part_kernel(RouterArgs a) {
+  constexpr int kPartWaveK = kRouterChunk / kPartWaves;  // hidden elements per wave
+  constexpr int kPartSteps = kPartWaveK / 32;            // matrix-core steps per wave
+  __shared__ float red[kPartWaves][kPartRows][NHB * 16 + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, c = lane & 15;
+  const int ch = blockIdx.x % a.nchunk, rb = blockIdx.x / a.nchunk;
+  const size_t pitch = static_cast<size_t>(a.d) * 2;  // bytes per row of x and of w
+  const char* xr = static_cast<const char*>(a.x) +
+                   static_cast<size_t>(min(rb * kPartRows + c, a.B - 1)) * pitch;
+  const char* wr[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+    wr[hb] = static_cast<const char*>(a.w) + static_cast<size_t>(min(hb * 16 + c, a.H - 1)) * pitch;
+  const int k0 = ch * kRouterChunk + wave * kPartWaveK + q * 8;
+  uint4 av[kPartSteps], bv[kPartSteps][NHB];
+#pragma unroll
+  for (int j = 0; j < kPartSteps; ++j) {
+    const int k = k0 + 32 * j;
+    const size_t off = static_cast<size_t>(k < a.d ? k : 0) * 2;
+    av[j] = ld16(xr + off);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) bv[j][hb] = ld16(wr[hb] + off);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  rf32x4 acc[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) acc[hb] = rf32x4{0.f, 0.f, 0.f, 0.f};
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int j = 0; j < kPartSteps; ++j) {
+    const bool in = k0 + 32 * j < a.d;
+    const uint4 x = in ? av[j] : zero;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) acc[hb] = mma16<DT>(x, in ? bv[j][hb] : zero, acc[hb]);
+  }
+  // Lane (q, c) holds rows 4q .. 4q+3 of head hb*16 + c.
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * q + r][hb * 16 + c] = acc[hb][r];
+  __syncthreads();
+  for (int p = threadIdx.x; p < kPartRows * NHB * 16; p += kPartWaves * 64) {
+    const int r = p / (NHB * 16), h = p % (NHB * 16);
+    const int row = rb * kPartRows + r;
+    if (row < a.B && h < a.H) {
+      float s = red[0][r][h];
+#pragma unroll
+      for (int w = 1; w < kPartWaves; ++w) s += red[w][r][h];
+      a.part[(static_cast<size_t>(row) * a.nchunk + ch) * a.H + h] = s;
+    }
+  }
+}
+
 // Sort key of head h with score x in the (score descending, index
 // ascending) order: a larger key ranks first.  NaN becomes -inf and -0
 // becomes +0 (equal floats, equal keys); the float's bits are mapped to an
@@ -129,19 +229,76 @@ __device__ __forceinline__ unsigned long long topk_key(float x, int h) {
 // in ascending order with a ballot prefix count.  SLOTS = heads per lane
 // (H <= 64 SLOTS), a compile-time count so that the loops have no
 // branches.
-template <int SLOTS>
+//
+// SUM (the K-split form, H <= 128): the row's scores are first formed from
+// its partials.  The 256 threads are G = 256 / H groups of H (one head per
+// thread); group g adds chunks g, g + G, ... in order, the G group sums are
+// added in group order, then the bias; the result is written to scores and
+// ranked from LDS.  With top_k = 0 only the scores are written.
+template <int SLOTS, bool SUM>
 __global__ __launch_bounds__(kTopkWaves * 64) void sha_router_topk_kernel(RouterArgs a) {
   constexpr int N = 64 * SLOTS;
   constexpr int Q = N / kTopkWaves;
+  constexpr int T = kTopkWaves * 64;
   __shared__ unsigned long long keys[N];
   __shared__ int part[kTopkWaves][N];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = blockIdx.x;
-  const float* srow = a.scores + static_cast<size_t>(b) * a.H;
+  if constexpr (SUM) {
+    static_assert(N <= kRouterSplitMaxH, "one head per thread of a group");
+    __shared__ float gsum[T];
+    __shared__ float srow[N];
+    const int G = T / a.H;
+    const int g = threadIdx.x / a.H, h = threadIdx.x - g * a.H;
+    // The bias is loaded with the partials, not after them.
+    const float bias = (a.bias && threadIdx.x < a.H) ? a.bias[threadIdx.x] : 0.f;
+    float s = 0.f;
+    if (g < G) {
+      const float* p = a.part + static_cast<size_t>(b) * a.nchunk * a.H + h;
+      const size_t st = static_cast<size_t>(G) * a.H;
+      int ch = g;
+      // Eight loads in flight, added in chunk order.
+      for (; ch + 7 * G < a.nchunk; ch += 8 * G) {
+        const float* pc = p + static_cast<size_t>(ch) * a.H;
+        float v[8];
 #pragma unroll
-  for (int i = 0; i < (N + kTopkWaves * 64 - 1) / (kTopkWaves * 64); ++i) {
-    const int h = threadIdx.x + kTopkWaves * 64 * i;
-    if (h < N) keys[h] = topk_key(h < a.H ? srow[h] : kNegInf, h);
+        for (int u = 0; u < 8; ++u) v[u] = pc[u * st];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int c = ch + u * G;
+          v[u] = c < a.nchunk ? p[static_cast<size_t>(c) * a.H] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+    }
+    gsum[threadIdx.x] = s;
+    __syncthreads();
+    if (threadIdx.x < N) {
+      float t = kNegInf;
+      if (threadIdx.x < a.H) {
+        t = 0.f;
+        for (int q = 0; q < G; ++q) t += gsum[q * a.H + threadIdx.x];
+        t += bias;
+        a.scores[static_cast<size_t>(b) * a.H + threadIdx.x] = t;
+      }
+      srow[threadIdx.x] = t;
+    }
+    if (a.top_k == 0) return;
+    __syncthreads();
+    if (threadIdx.x < N) keys[threadIdx.x] = topk_key(srow[threadIdx.x], threadIdx.x);
+  } else {
+    const float* srow = a.scores + static_cast<size_t>(b) * a.H;
+#pragma unroll
+    for (int i = 0; i < (N + T - 1) / T; ++i) {
+      const int h = threadIdx.x + T * i;
+      if (h < N) keys[h] = topk_key(h < a.H ? srow[h] : kNegInf, h);
+    }
   }
   __syncthreads();
   unsigned long long mine[SLOTS];
@@ -176,11 +333,37 @@ __global__ __launch_bounds__(kTopkWaves * 64) void sha_router_topk_kernel(Router
   }
 }
 
-template <int SLOTS>
+template <int SLOTS, bool SUM = false>
 hipError_t launch_topk(const RouterArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((sha_router_topk_kernel<SLOTS>), dim3(static_cast<unsigned>(a.B)),
+  hipLaunchKernelGGL((sha_router_topk_kernel<SLOTS, SUM>), dim3(static_cast<unsigned>(a.B)),
                      dim3(kTopkWaves * 64), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DT, int NHB>
+void launch_part(const RouterArgs& a, hipStream_t st) {
+  const long long wgs = static_cast<long long>(a.nchunk) * ((a.B + kPartRows - 1) / kPartRows);
+  hipLaunchKernelGGL((sha_router_part_kernel<DT, NHB>), dim3(static_cast<unsigned>(wgs)),
+                     dim3(kPartWaves * 64), 0, st, a);
+}
+
+// K-split form: partials, then the summing top-k kernel (always launched:
+// it writes the scores).
+template <int DT>
+hipError_t launch_router_split(const RouterArgs& a, hipStream_t st) {
+  switch ((a.H + 15) / 16) {
+    case 1: launch_part<DT, 1>(a, st); break;
+    case 2: launch_part<DT, 2>(a, st); break;
+    case 3: launch_part<DT, 3>(a, st); break;
+    case 4: launch_part<DT, 4>(a, st); break;
+    case 5: launch_part<DT, 5>(a, st); break;
+    case 6: launch_part<DT, 6>(a, st); break;
+    case 7: launch_part<DT, 7>(a, st); break;
+    default: launch_part<DT, 8>(a, st); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.H <= 64 ? launch_topk<1, true>(a, st) : launch_topk<2, true>(a, st);
 }
 
 template <int DT, int HEADS>
@@ -192,6 +375,9 @@ void launch_scores(const RouterArgs& a, hipStream_t st) {
 
 template <int DT>
 hipError_t launch_router_t(const RouterArgs& a, int num_cus, hipStream_t st) {
+  if constexpr (DT != kF32) {
+    if (a.part) return launch_router_split<DT>(a, st);
+  }
   // 4 heads per workgroup; 2 when that leaves CUs idle (small batches or
   // few heads), trading more reads of the row for more workgroups.
   if (static_cast<long long>(a.B) * ((a.H + 3) / 4) < num_cus)

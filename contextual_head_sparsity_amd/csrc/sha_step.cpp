@@ -15,8 +15,9 @@ struct sha_step {
   std::vector<sha_step_layer> layers;
   std::vector<sha_kv_layout> kv;       // per layer copy of the caller's layout
   std::vector<int> nsplit;             // per layer split count (fixed at create)
-  void* attn_ws = nullptr;
-  size_t attn_ws_bytes = 0;
+  void* attn_ws = nullptr;              // SHA split partials; also the router's K-split
+  size_t attn_ws_bytes = 0;              // partials (the router runs first on the stream)
+  size_t router_ws_bytes = 0;
   int32_t* dense_index = nullptr;      // [B, H or H_kv] = 0 .. n-1 per row
   int32_t* sel = nullptr;              // MLP union output [max(1, n_max)]
   int32_t* n_sel = nullptr;
@@ -62,8 +63,9 @@ sha_status enqueue(sha_step* s, hipStream_t stream) {
       index = s->dense_index;
       top_k = n_sel_heads;
     } else {
-      st = sha_router_topk(L.router_x, L.router_w, L.router_bias, c.B, c.router_d, n_sel_heads,
-                           top_k, L.index, L.router_scores, stream, c.dtype);
+      st = sha_router_topk_ex(L.router_x, L.router_w, L.router_bias, c.B, c.router_d,
+                              n_sel_heads, top_k, L.index, L.router_scores, stream, c.dtype,
+                              s->router_ws_bytes ? s->attn_ws : nullptr, s->attn_ws_bytes);
       if (st != SHA_OK) return st;
     }
     st = c.gqa ? sha_decode_gqa_kv(L.q, L.k, L.v, index, c.B, c.H, c.H_kv, c.Nkv, c.d, top_k,
@@ -116,6 +118,8 @@ sha_status create(const sha_step_config* cfg, const sha_step_layer* layers, int 
     if (ws > s->attn_ws_bytes) s->attn_ws_bytes = ws;
     any_mlp = any_mlp || has_mlp(L);
   }
+  s->router_ws_bytes = sha_router_workspace_bytes(c.B, c.router_d, n_sel_heads, c.dtype);
+  if (s->router_ws_bytes > s->attn_ws_bytes) s->attn_ws_bytes = s->router_ws_bytes;
   sha_status st = dev_alloc(&s->attn_ws, s->attn_ws_bytes);
   if (st != SHA_OK) return st;
 

@@ -284,6 +284,34 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
                            hipStream_t stream, sha_dtype dtype);
 
 /*
+ * The same router with a caller workspace, which lets 16-bit calls of up to
+ * 128 heads and 4096 rows split the hidden dimension: matrix-core partial
+ * products per 256 hidden elements (fp32), added per row in a fixed order by
+ * the top-k kernel; two launches as before, the first of many short
+ * workgroups.  Results are those of sha_router_topk up to fp32 rounding
+ * order; a call repeated on the same inputs returns the same bits.
+ *   sha_router_split_bytes: bytes the split form needs for this shape,
+ *     B * ceil(d / 256) * H * 4 rounded up to 256; 0 when the shape has no
+ *     split form (f32, H > 128, B > 4096, d not a multiple of 8, B < 1).
+ *   sha_router_workspace_bytes: the same where the split form is the faster
+ *     one (B * H * d >= 2^24 multiply-adds), else 0.  Callers pass a
+ *     workspace of that size, or null when it is 0.
+ *   workspace: device memory, 16-byte aligned (SHA_ERR_MISALIGNED), owned by
+ *     the caller; its contents on entry do not matter.  On a shape with a
+ *     split form a non-null workspace selects that form and must hold
+ *     sha_router_split_bytes (SHA_ERR_WORKSPACE); otherwise, or when null,
+ *     the one-pass kernels of sha_router_topk run and it is not touched.
+ *     Calls that may overlap (several streams) need separate workspaces.
+ * Other arguments, limits and errors as sha_router_topk.
+ */
+size_t sha_router_split_bytes(int B, int d, int H, sha_dtype dtype);
+size_t sha_router_workspace_bytes(int B, int d, int H, sha_dtype dtype);
+sha_status sha_router_topk_ex(const void* x, const void* w, const float* bias, int B, int d,
+                              int H, int top_k, int32_t* batch_head_index, float* scores,
+                              hipStream_t stream, sha_dtype dtype, void* workspace,
+                              size_t workspace_bytes);
+
+/*
  * Selective MLP ("Selective GEMM") over the batch union of active neurons.
  * Polar Sparsity notes (papernotes.org), 方法详解 > 关键设计 > "MLP 层动态稀疏":
  * MLP_{S_B}(x) = sigma(x W1[:, S_B]) W2[:, S_B]^T, where S_B is the union of

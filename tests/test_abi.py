@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_header_symbols_exported_and_bound():
     names = _declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 30, names
     L = ctypes.CDLL(bd.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -216,6 +216,37 @@ def test_router_host_validation():
     # the scores grid: B * ceil(H / 2) workgroups, at most 2^22
     assert r(B=(1 << 22) // 36 + 1) == 1 and r(B=(1 << 22) // 36, x=None) == 1
     assert r(B=1 << 22, H=1, k=1, x=None) == 1 and r(B=(1 << 22) + 1, H=1, k=1) == 1
+
+
+def test_router_workspace_accounting_and_validation():
+    """The K-split form's workspace: one fp32 partial per (row, 512 hidden
+    elements, head), 256-byte rounded; 0 for shapes without the form.  Errors
+    are raised on the host before any launch (fake device addresses)."""
+    L = bd.lib()
+    P = A16
+    sb, wsb = L.sha_router_split_bytes, L.sha_router_workspace_bytes
+    assert sb(64, 9216, 72, 1) == 64 * 36 * 72 * 4
+    assert sb(16, 4096, 32, 2) == 16 * 16 * 32 * 4
+    assert sb(3, 264, 5, 1) == (3 * 2 * 5 * 4 + 255) // 256 * 256     # ragged last chunk
+    assert sb(4096, 512, 128, 2) == 4096 * 2 * 128 * 4
+    for args in [(64, 9216, 72, 0),       # f32: one-pass only
+                 (64, 9216, 129, 1),      # more than 128 heads
+                 (4097, 512, 8, 1),       # more than 4096 rows
+                 (0, 512, 8, 1), (4, 12, 8, 1), (4, 512, 8, 7)]:
+        assert sb(*args) == 0 and wsb(*args) == 0, args
+    # the library's pick: the split form from 2^24 multiply-adds per call
+    assert wsb(64, 9216, 72, 1) == sb(64, 9216, 72, 1)          # OPT-66B layer
+    assert wsb(128, 4096, 32, 2) == sb(128, 4096, 32, 2)        # exactly 2^24
+    assert wsb(127, 4096, 32, 2) == 0 and wsb(16, 4096, 32, 1) == 0 and wsb(64, 8192, 8, 2) == 0
+
+    def r(ws=P, ws_bytes=1 << 20, B=4, d=256, H=72, k=22, dtype=1, x=P):
+        return L.sha_router_topk_ex(x, P, None, B, d, H, k, P, P, None, dtype, ws, ws_bytes)
+
+    need = sb(4, 256, 72, 1)
+    assert r(ws_bytes=need - 1) == 4 and r(ws=P + 8) == 3
+    assert r(k=73) == 1 and r(x=P + 8) == 3 and r(B=0, x=None, ws=None) == 0
+    # shapes without the split form ignore the workspace, even a short one
+    assert r(ws_bytes=0, H=200, x=P + 8) == 3 and r(ws_bytes=0, dtype=0, x=P + 4) == 3
 
 
 def _kv_layout(**kw):

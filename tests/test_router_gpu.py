@@ -19,6 +19,7 @@ from oracle import router_scores_ref, sha_decode_gqa_ref, sha_decode_ref, to_f64
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+ROUTER_CHUNK = 256   # hidden elements per K-split partial
 
 
 def say(m):
@@ -180,3 +181,68 @@ def test_router_graph_replays(warm):
         i2, s2 = sha.router_topk(x2.to(DEV), w2.to(DEV), k, bias=b2.to(DEV), stream=s)
         s.synchronize()
         _check(x2, w2, b2, k, i2, s2)
+
+
+# The K-split form (16-bit, H <= 128, B <= 4096): row blocks of 16 with a
+# ragged last block, head blocks of 16 with a partial last block (1 ... 8
+# blocks), hidden widths whose last 512-element chunk is partial (down to one
+# 8-element piece), one chunk only, and top_k = 0 (scores only).
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B,d,H,k", [(64, 9216, 72, 22), (16, 4096, 32, 16), (128, 4096, 32, 16),
+                                     (64, 8192, 8, 5), (17, 520, 128, 40), (1, 8, 1, 1),
+                                     (33, 1032, 65, 64), (5, 512, 17, 0), (300, 2056, 100, 7),
+                                     (4096, 64, 8, 2)])
+def test_router_split_form_matches_oracle(dtype, B, d, H, k):
+    say(f"[router split] {dtype} B={B} d={d} H={H} k={k}")
+    dt = DT[dtype]
+    need = sha.router_workspace_bytes(B, d, H, dt, split=True)
+    assert need == (B * -(-d // ROUTER_CHUNK) * H * 4 + 255) // 256 * 256
+    x, w, b = _inputs(B, d, H, dtype, seed=B * 11 + H + d)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)   # contents do not matter
+    idx, sc = sha.router_topk(xd, wd, k, bias=bd, workspace=ws, split=True)
+    torch.cuda.synchronize()
+    _check(x, w, b, k, idx, sc)
+    # the same inputs again: the same bits (fixed summation order)
+    idx2, sc2 = sha.router_topk(xd, wd, k, bias=bd, split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(sc, sc2)
+    # the one-pass kernels agree with the oracle too
+    idx1, sc1 = sha.router_topk(xd, wd, k, bias=bd, split=False)
+    torch.cuda.synchronize()
+    _check(x, w, b, k, idx1, sc1)
+
+
+def test_router_split_raw_entry_points():
+    """sha_router_topk_ex through the C ABI: an explicit workspace gives the
+    binding's result; a short one is refused before any launch and leaves the
+    outputs untouched; no workspace runs the one-pass kernels."""
+    say("[router split] raw C ABI")
+    L = sha.lib()
+    B, d, H, k = 24, 3072, 72, 22
+    x, w, b = _inputs(B, d, H, "f16", seed=77)
+    xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
+    need = L.sha_router_split_bytes(B, d, H, 1)
+    assert need == B * 12 * H * 4
+    assert L.sha_router_workspace_bytes(B, d, H, 1) == 0     # below 2^24 multiply-adds
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    idx = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
+    sc = torch.full((B, H), 3.0, dtype=torch.float32, device=DEV)
+    s = torch.cuda.current_stream(DEV).cuda_stream
+    st = L.sha_router_topk_ex(xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), B, d, H, k,
+                              idx.data_ptr(), sc.data_ptr(), s, 1, ws.data_ptr(), need - 4)
+    torch.cuda.synchronize()
+    assert st == 4 and (idx == -7).all() and (sc == 3.0).all()
+    st = L.sha_router_topk_ex(xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), B, d, H, k,
+                              idx.data_ptr(), sc.data_ptr(), s, 1, ws.data_ptr(), need)
+    torch.cuda.synchronize()
+    assert st == 0
+    _check(x, w, b, k, idx, sc)
+    bidx, bsc = sha.router_topk(xd, wd, k, bias=bd, split=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, bidx) and torch.equal(sc, bsc)
+    st = L.sha_router_topk(xd.data_ptr(), wd.data_ptr(), bd.data_ptr(), B, d, H, k,
+                           idx.data_ptr(), sc.data_ptr(), s, 1)
+    torch.cuda.synchronize()
+    assert st == 0
+    _check(x, w, b, k, idx, sc)

@@ -196,6 +196,11 @@ CASES = {
     "mha_f32_d64": (dict(B=3, H=6, H_kv=6, d=64, Nkv=2100, top_k=2, gqa=False,
                          dtype=torch.float32, dname="f32", router_d=128),
                     None, 1, None),
+    # B * H * router_d = 2^24: the router takes its K-split form, its partials
+    # in the step's attention workspace
+    "mha_bf16_split_router": (dict(B=64, H=8, H_kv=8, d=64, Nkv=130, top_k=3, gqa=False,
+                                   dtype=torch.bfloat16, dname="bf16", router_d=32768),
+                              None, 2, None),
 }
 
 
