@@ -10,8 +10,9 @@ for bitwise determinism.  Rows past a row's length are NaN in the cache, so
 a read beyond it shows.  Two smaller sweeps do the same for the selective MLP
 (batch rows over one to three 64-row tiles, widths and neuron counts across
 the 128-neuron and 256-column tiles, empty and padded selections) and the
-router (1-1024 heads, ragged hidden widths, top_k from 0 to H), with the
-tolerances of their own GPU test files."""
+router (1-1024 heads, ragged hidden widths, top_k from 0 to H; the K-split
+form forced too wherever the shape has one), with the tolerances of their
+own GPU test files."""
 import os
 
 import numpy as np
@@ -204,7 +205,14 @@ def test_mixed_router(i):
     dtype, B, d, H, k, bias = _router_case(i)
     say(f"[mixed router {i}] {dtype} B={B} d={d} H={H} k={k} bias={bias}")
     x, w, b = _inputs(B, d, H, dtype, seed=800 + i, bias=bias)
-    idx, sc = sha.router_topk(x.to(DEV), w.to(DEV), k, bias=b.to(DEV) if b is not None else None)
+    bd = b.to(DEV) if b is not None else None
+    idx, sc = sha.router_topk(x.to(DEV), w.to(DEV), k, bias=bd)
     torch.cuda.synchronize()
     exact = _check(x, w, b, k, idx, sc)
     say(f"   rows with an exact set check: {exact}/{B}")
+    if sha.router_workspace_bytes(B, d, H, x.dtype, split=True) > 0:
+        # the K-split form forced on the same case
+        idx2, sc2 = sha.router_topk(x.to(DEV), w.to(DEV), k, bias=bd, split=True)
+        torch.cuda.synchronize()
+        _check(x, w, b, k, idx2, sc2)
+        say("   K-split form checked too")
