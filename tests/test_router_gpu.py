@@ -185,13 +185,14 @@ def test_router_graph_replays(warm):
 
 # The K-split form (16-bit, H <= 128, B <= 4096): row blocks of 16 with a
 # ragged last block, head blocks of 16 with a partial last block (1 ... 8
-# blocks), hidden widths whose last 512-element chunk is partial (down to one
-# 8-element piece), one chunk only, and top_k = 0 (scores only).
+# blocks), hidden widths whose last 256-element chunk is partial (down to one
+# 8-element piece), one chunk only, top_k = 0 (scores only), and the largest
+# shape it takes (4096 rows x 128 heads).
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("B,d,H,k", [(64, 9216, 72, 22), (16, 4096, 32, 16), (128, 4096, 32, 16),
                                      (64, 8192, 8, 5), (17, 520, 128, 40), (1, 8, 1, 1),
                                      (33, 1032, 65, 64), (5, 512, 17, 0), (300, 2056, 100, 7),
-                                     (4096, 64, 8, 2)])
+                                     (4096, 64, 8, 2), (4096, 264, 128, 64)])
 def test_router_split_form_matches_oracle(dtype, B, d, H, k):
     say(f"[router split] {dtype} B={B} d={d} H={H} k={k}")
     dt = DT[dtype]
