@@ -800,7 +800,9 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
 
 size_t sha_router_split_bytes(int B, int d, int H, sha_dtype dtype) {
   if (dtype != SHA_F16 && dtype != SHA_BF16) return 0;
-  if (B < 1 || d < 8 || d % 8 != 0 || H < 1 || H > sha::kRouterSplitMaxH ||
+  // d <= 2^30 keeps the kernel's 32-bit hidden offsets and its grid
+  // (ceil(B / 16) * ceil(d / 256) workgroups) in range.
+  if (B < 1 || d < 8 || d % 8 != 0 || d > (1 << 30) || H < 1 || H > sha::kRouterSplitMaxH ||
       B > sha::kRouterSplitMaxB)
     return 0;
   const size_t nchunk = (static_cast<size_t>(d) + sha::kRouterChunk - 1) / sha::kRouterChunk;

@@ -292,7 +292,8 @@ sha_status sha_router_topk(const void* x, const void* w, const float* bias, int 
  * order; a call repeated on the same inputs returns the same bits.
  *   sha_router_split_bytes: bytes the split form needs for this shape,
  *     B * ceil(d / 256) * H * 4 rounded up to 256; 0 when the shape has no
- *     split form (f32, H > 128, B > 4096, d not a multiple of 8, B < 1).
+ *     split form (f32, H > 128, B > 4096, d not a multiple of 8 or above
+ *     2^30, B < 1).
  *   sha_router_workspace_bytes: the same where the split form is the faster
  *     one (B * H * d >= 2^24 multiply-adds), else 0.  Callers pass a
  *     workspace of that size, or null when it is 0.

@@ -232,7 +232,8 @@ def test_router_workspace_accounting_and_validation():
     for args in [(64, 9216, 72, 0),       # f32: one-pass only
                  (64, 9216, 129, 1),      # more than 128 heads
                  (4097, 512, 8, 1),       # more than 4096 rows
-                 (0, 512, 8, 1), (4, 12, 8, 1), (4, 512, 8, 7)]:
+                 (0, 512, 8, 1), (4, 12, 8, 1), (4, 512, 8, 7),
+                 (4096, (1 << 30) + 8, 8, 1)]:   # hidden width past 2^30
         assert sb(*args) == 0 and wsb(*args) == 0, args
     # the library's pick: the split form from 2^24 multiply-adds per call
     assert wsb(64, 9216, 72, 1) == sb(64, 9216, 72, 1)          # OPT-66B layer
