@@ -150,12 +150,34 @@ def _stream_for(dev, stream):
     return torch.cuda.current_stream(dev) if stream is None else stream
 
 
+def _on(t, dev, name):
+    """t must be a tensor on device dev (a host tensor's address would reach
+    a kernel as a device address)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+    return t
+
+
+def _workspace(ws, need, dev):
+    """The caller's workspace (a contiguous tensor on dev), or a new one when
+    none is given or it is shorter than need bytes."""
+    if ws is not None:
+        _on(ws, dev, "workspace")
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if ws.numel() * ws.element_size() >= need:
+            return ws
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+
 def _prepare(q, k, v, index, scale, out, gqa, paged=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     for name, t in (("k", k), ("v", v)):
@@ -195,13 +217,13 @@ def _layout(k, v, seqlens, block_table, B, Nkv):
     keep = []
     lay = KvLayout(k.stride(0), k.stride(1), k.stride(2), v.stride(0), v.stride(1), v.stride(2))
     if seqlens is not None:
-        seqlens = _dev_i32(seqlens, "seqlens")
+        seqlens = _dev_i32(_on(seqlens, k.device, "seqlens"), "seqlens")
         if seqlens.numel() != B:
             raise ValueError("seqlens must hold B entries")
         lay.seqlens = seqlens.data_ptr()
         keep.append(seqlens)
     if block_table is not None:
-        bt = _dev_i32(block_table, "block_table")
+        bt = _dev_i32(_on(block_table, k.device, "block_table"), "block_table")
         if bt.dim() != 2 or bt.shape[0] != B:
             raise ValueError("block_table must be [B, max_pages]")
         lay.block_table = bt.data_ptr()
@@ -233,9 +255,7 @@ def _call(gqa, q, k, v, index, scale, out, nsplit, workspace, stream, seqlens=No
         dt = _DT[q.dtype]
         lp = ctypes.byref(lay) if lay is not None else None
         need = L.sha_workspace_bytes_kv(B, H, H_kv, Nkv, d, top_k, int(gqa), dt, nsplit, 0, lp)
-        if need and (workspace is None or not workspace.is_cuda or
-                     workspace.numel() * workspace.element_size() < need):
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, need, q.device) if need else None
         ws_ptr = workspace.data_ptr() if need else None
         with torch.cuda.device(q.device):
             if lay is None:
@@ -326,13 +346,16 @@ def mlp_union(row_neurons, D, sel=None, n_sel=None, stream=None, workspace=None)
         cap = max(1, min(D, B * k))
         if sel is None:
             sel = torch.empty(cap, dtype=torch.int32, device=rows.device)
-        elif sel.numel() < cap or sel.dtype != torch.int32 or not sel.is_contiguous():
+        elif (_on(sel, rows.device, "sel").numel() < cap or sel.dtype != torch.int32
+              or not sel.is_contiguous()):
             raise ValueError(f"sel must be a contiguous int32 tensor of >= {cap} entries")
         if n_sel is None:
             n_sel = torch.empty(1, dtype=torch.int32, device=rows.device)
+        elif (_on(n_sel, rows.device, "n_sel").numel() < 1 or n_sel.dtype != torch.int32
+              or not n_sel.is_contiguous()):
+            raise ValueError("n_sel must be a contiguous int32 tensor of >= 1 entry")
         need = lib().sha_mlp_union_workspace_bytes(D)
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=rows.device)
+        workspace = _workspace(workspace, need, rows.device)
         with torch.cuda.device(rows.device):
             st = lib().sha_mlp_union(rows.data_ptr(), B, k, D, sel.data_ptr(), n_sel.data_ptr(),
                                      stream.cuda_stream, workspace.data_ptr(), need)
@@ -360,22 +383,26 @@ def selective_mlp(x, w1t, w2t, sel, n_sel, n_max=None, out=None, workspace=None,
     D = w1t.shape[0]
     if w1t.shape != (D, d) or w2t.shape != (D, d):
         raise ValueError("w1t and w2t must be [D, d]")
+    if w1t.device != x.device or w2t.device != x.device:
+        raise ValueError("x, w1t, w2t must be on one device")
     stream = _stream_for(x.device, stream)
     with torch.cuda.stream(stream):
-        sel = _dev_i32(sel, "sel")
-        n_sel = _dev_i32(n_sel, "n_sel")
+        sel = _dev_i32(_on(sel, x.device, "sel"), "sel")
+        n_sel = _dev_i32(_on(n_sel, x.device, "n_sel"), "n_sel")
+        if n_sel.numel() < 1:
+            raise ValueError("n_sel must hold the count")
         if n_max is None:
             n_max = min(sel.numel(), D)
         if n_max > sel.numel():
             raise ValueError(f"n_max = {n_max} exceeds the {sel.numel()} entries of sel")
         if out is None:
             out = torch.empty_like(x)
-        elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        elif (_on(out, x.device, "out").shape != x.shape or out.dtype != x.dtype
+              or not out.is_contiguous()):
             raise ValueError("out must be a contiguous tensor like x")
         L = lib()
         need = L.sha_selective_mlp_workspace_bytes(B, d, D, n_max, 0)
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _workspace(workspace, need, x.device)
         with torch.cuda.device(x.device):
             st = L.sha_selective_mlp(x.data_ptr(), w1t.data_ptr(), w2t.data_ptr(), sel.data_ptr(),
                                      n_sel.data_ptr(), n_max, B, d, D, out.data_ptr(),
@@ -415,25 +442,27 @@ def router_topk(x, w, top_k, bias=None, index=None, scores=None, stream=None, wo
     H = w.shape[0]
     if w.shape[1] != d:
         raise ValueError("w must be [H, d]")
+    if w.device != x.device:
+        raise ValueError("x and w must be on one device")
     stream = _stream_for(x.device, stream)
     with torch.cuda.stream(stream):
         if bias is not None:
-            if not bias.is_cuda or bias.dtype != torch.float32 or bias.numel() != H:
+            if _on(bias, x.device, "bias").dtype != torch.float32 or bias.numel() != H:
                 raise ValueError("bias must be a float32 device tensor of H entries")
             bias = bias.contiguous()
         if index is None:
             index = torch.empty((B, top_k), dtype=torch.int32, device=x.device)
-        elif index.dtype != torch.int32 or not index.is_contiguous() or \
+        elif _on(index, x.device, "index").dtype != torch.int32 or not index.is_contiguous() or \
                 tuple(index.shape) != (B, top_k):
             raise ValueError("index must be a contiguous int32 [B, top_k] tensor")
         if scores is None:
             scores = torch.empty((B, H), dtype=torch.float32, device=x.device)
-        elif scores.dtype != torch.float32 or not scores.is_contiguous() or \
-                tuple(scores.shape) != (B, H):
+        elif _on(scores, x.device, "scores").dtype != torch.float32 or \
+                not scores.is_contiguous() or tuple(scores.shape) != (B, H):
             raise ValueError("scores must be a contiguous float32 [B, H] tensor")
         need = router_workspace_bytes(B, d, H, x.dtype, split)
-        if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if need > 0:
+            workspace = _workspace(workspace, need, x.device)
         with torch.cuda.device(x.device):
             st = lib().sha_router_topk_ex(x.data_ptr(), w.data_ptr(),
                                           bias.data_ptr() if bias is not None else None, B, d, H,
@@ -504,8 +533,10 @@ class DecodeStep:
                          "k", "v", "o", "mlp_x", "mlp_w1t", "mlp_w2t", "mlp_y", "mlp_rows"):
                 t = L.get(name)
                 if t is not None:
-                    if not t.is_cuda:
-                        raise ValueError(f"layer {i}: {name} must be a device tensor")
+                    if not isinstance(t, torch.Tensor) or not t.is_cuda or \
+                            t.device != layers[0]["q"].device:
+                        raise ValueError(f"layer {i}: {name} must be a tensor on the device of "
+                                         "layer 0's q")
                     self._keep.append(t)
                 setattr(arr[i], name, _ptr(t))
             arr[i].dense = int(bool(L.get("dense", False)))

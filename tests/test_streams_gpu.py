@@ -4,6 +4,8 @@
   is still busy: the binding makes its temporaries (the int32 index copy,
   the zero-filled output, the workspace) on the call's stream, so the result
   matches the fp64 oracle.
+* Host tensors passed where the library expects device memory (outputs,
+  index and count buffers, workspaces) are refused by the binding.
 * The internal-workspace entry points on a stream under capture: a call
   that would have to grow the workspace returns SHA_ERR_WORKSPACE and
   enqueues nothing; once the workspace exists, the call is captured and
@@ -95,6 +97,60 @@ def test_selective_mlp_rejects_n_max_beyond_selection():
     n_sel = torch.full((1,), 8, dtype=torch.int32, device=DEV)
     with pytest.raises(ValueError, match="n_max"):
         sha.selective_mlp(x, w1t, w2t, sel, n_sel, n_max=9)
+
+
+def test_binding_rejects_host_buffers():
+    """Every output, index and workspace argument the binding passes to the
+    library as a device address must be a tensor on the call's device: a
+    host tensor is refused with ValueError before the library enqueues
+    anything, and the device outputs stay as they were."""
+    say("[binding] host buffers refused")
+    host = torch.empty(1 << 20, dtype=torch.uint8)
+    w, q, k, v, idx, o = _case(B=2, Nkv=3000)
+    qd, kd, vd, idd = q.to(DEV), k.to(DEV), v.to(DEV), idx.to(DEV)
+    assert sha.workspace_bytes(2, w.H, w.H_kv, 3000, w.d, w.top_k, dtype=qd.dtype, nsplit=4) > 0
+    od = torch.full_like(qd, 5.0)
+    with pytest.raises(ValueError, match="out"):
+        sha.sha_decode(qd, kd, vd, idd, out=o)
+    with pytest.raises(ValueError, match="workspace"):
+        sha.sha_decode(qd, kd, vd, idd, out=od, nsplit=4, workspace=host)
+    with pytest.raises(ValueError, match="device"):
+        sha.sha_decode(qd, k, vd, idd, out=od)
+    with pytest.raises(ValueError, match="seqlens"):
+        sha.sha_decode(qd, kd, vd, idd, out=od,
+                       seqlens=torch.full((2,), 64, dtype=torch.int32))
+    torch.cuda.synchronize()
+    assert (od == 5.0).all()
+    # router: index, scores, bias, workspace
+    x = torch.randn(64, 9216, device=DEV).half()
+    rw = torch.randn(72, 9216, device=DEV).half()
+    idx_d = torch.full((64, 22), -5, dtype=torch.int32, device=DEV)
+    sc_d = torch.full((64, 72), 7.0, device=DEV)
+    for kw, what in [(dict(index=torch.empty(64, 22, dtype=torch.int32)), "index"),
+                     (dict(scores=torch.empty(64, 72)), "scores"),
+                     (dict(bias=torch.zeros(72)), "bias"),
+                     (dict(workspace=host, index=idx_d, scores=sc_d), "workspace")]:
+        with pytest.raises(ValueError, match=what):
+            sha.router_topk(x, rw, 22, **kw)
+    torch.cuda.synchronize()
+    assert (idx_d == -5).all() and (sc_d == 7.0).all()
+    # union and selective MLP: sel, n_sel, out, workspace
+    mw = wl.MlpWorkload("host", B=2, d=256, D=300, k_row=4, dtype="f16", seed=1)
+    xm, w1t, w2t, rows = wl.make_mlp(mw, DEV)
+    sel, n_sel = sha.mlp_union(rows, mw.D)
+    for kw, what in [(dict(sel=torch.empty(8, dtype=torch.int32)), "sel"),
+                     (dict(n_sel=torch.empty(1, dtype=torch.int32)), "n_sel"),
+                     (dict(workspace=host), "workspace")]:
+        with pytest.raises(ValueError, match=what):
+            sha.mlp_union(rows, mw.D, **kw)
+    y = torch.full_like(xm, 3.0)
+    for args, kw, what in [((sel.cpu(), n_sel), {}, "sel"), ((sel, n_sel.cpu()), {}, "n_sel"),
+                           ((sel, n_sel), dict(out=torch.empty(2, 256, dtype=torch.half)), "out"),
+                           ((sel, n_sel), dict(out=y, workspace=host), "workspace")]:
+        with pytest.raises(ValueError, match=what):
+            sha.selective_mlp(xm, w1t, w2t, *args, **kw)
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
 
 
 def test_internal_workspace_under_capture():
