@@ -80,14 +80,16 @@ def test_router_matches_oracle(dtype, B, d, H, k):
     say(f"   rows with an exact set check: {exact}/{B}")
 
 
-def test_router_ties_and_nan():
-    """Equal scores pick the lowest heads; NaN scores rank last."""
+@pytest.mark.parametrize("split", [False, True])
+def test_router_ties_and_nan(split):
+    """Equal scores pick the lowest heads; NaN scores rank last (one-pass and
+    K-split forms)."""
     x = torch.ones(2, 64, dtype=torch.float16)
     w = torch.zeros(10, 64, dtype=torch.float16)
     w[7] = 1.0                                   # head 7 scores 64, the rest 0
     b = torch.zeros(10)
     b[3] = float("nan")
-    idx, sc = sha.router_topk(x.to(DEV), w.to(DEV), 4, bias=b.to(DEV))
+    idx, sc = sha.router_topk(x.to(DEV), w.to(DEV), 4, bias=b.to(DEV), split=split)
     torch.cuda.synchronize()
     assert idx.cpu().tolist() == [[0, 1, 2, 7], [0, 1, 2, 7]]
     assert torch.isnan(sc[:, 3]).all()
@@ -144,12 +146,14 @@ def test_router_consecutive_calls_and_streams():
         _check(x, w, b, k, idx, sc)
 
 
+@pytest.mark.parametrize("split", [None, True])
 @pytest.mark.parametrize("warm", [False, True])
-def test_router_graph_replays(warm):
+def test_router_graph_replays(warm, split):
     """A router call captured in a graph, on a fresh or an already used
     stream: each replay (with eager router calls on the same stream in
-    between) matches the eager result bit for bit and the oracle."""
-    say(f"[router] graph replays warm={warm}")
+    between) matches the eager result bit for bit and the oracle; the
+    K-split form's temporary workspace is captured with the call."""
+    say(f"[router] graph replays warm={warm} split={split}")
     B, d, H, k = 48, 2048, 72, 22
     x, w, b = _inputs(B, d, H, "f16", seed=7)
     xd, wd, bd = x.to(DEV), w.to(DEV), b.to(DEV)
@@ -158,11 +162,11 @@ def test_router_graph_replays(warm):
     idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
     sc = torch.empty((B, H), dtype=torch.float32, device=DEV)
     if warm:
-        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s)
+        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s, split=split)
         s.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s)
+        sha.router_topk(xd, wd, k, bias=bd, index=idx, scores=sc, stream=s, split=split)
     torch.cuda.synchronize()
     x2, w2, b2 = _inputs(B, d, H, "f16", seed=8)
     eager_idx, eager_sc = None, None
@@ -174,11 +178,12 @@ def test_router_graph_replays(warm):
         torch.cuda.synchronize()
         _check(x, w, b, k, idx, sc)
         if eager_idx is None:
-            eager_idx, eager_sc = sha.router_topk(xd, wd, k, bias=bd, stream=s)
+            eager_idx, eager_sc = sha.router_topk(xd, wd, k, bias=bd, stream=s, split=split)
             s.synchronize()
         assert torch.equal(idx, eager_idx) and torch.equal(sc, eager_sc)
         # other work on the captured stream between replays
-        i2, s2 = sha.router_topk(x2.to(DEV), w2.to(DEV), k, bias=b2.to(DEV), stream=s)
+        i2, s2 = sha.router_topk(x2.to(DEV), w2.to(DEV), k, bias=b2.to(DEV), stream=s,
+                                 split=split)
         s.synchronize()
         _check(x2, w2, b2, k, i2, s2)
 
