@@ -10,7 +10,9 @@
  * 2. The sparse layer's other calls, on exact inputs: the attention router
  *    with unit-vector weight rows (scores = the hidden state's first H
  *    entries, so the top-k is known), its index then used for a decode
- *    call; the batch union of the rows' neuron lists (with -1 padding); and
+ *    call; the router's K-split form with a caller workspace (f16 small
+ *    integers over two hidden chunks, exact scores and top-k); the batch
+ *    union of the rows' neuron lists (with -1 padding); and
  *    the selective MLP on small integers (x in {0, 1}, weights in
  *    {-1, 0, 1}), whose every intermediate and output is an integer that
  *    f16 and fp32 hold exactly, so the check is equality.
@@ -300,6 +302,84 @@ static int run_mlp(void) {
   return ok;
 }
 
+/* f16 bit pattern of a small integer (|n| < 2048: exact). */
+static uint16_t f16_bits(int n) {
+  if (n == 0) return 0;
+  const uint16_t sign = n < 0 ? 0x8000u : 0u;
+  unsigned m = (unsigned)(n < 0 ? -n : n);
+  int e = 0;
+  while ((m >> (e + 1)) != 0) ++e;
+  return (uint16_t)(sign | (unsigned)(15 + e) << 10 | ((m - (1u << e)) << (10 - e)));
+}
+
+/* The router's K-split form through sha_router_topk_ex with a hipMalloc'd
+ * workspace of sha_router_split_bytes: f16 hidden states of small integers
+ * over 264 hidden elements (two 256-element chunks, the second holding one
+ * 8-element piece); head h's weight row holds 1 at elements h and 256 + h,
+ * so scores[b, h] = x[b, h] + x[b, 256 + h] exactly, a sum of the two
+ * chunks' partials. */
+static int run_router_split(void) {
+  enum { B = 2, D = 264, H = 6, K = 3 };
+  const int xa[B][H] = {{1, 5, -2, 7, 0, 3}, {4, -1, 6, 2, 9, 2}};   /* elements 0..5 */
+  const int xb[B][H] = {{2, -1, 8, 0, 1, 3}, {0, 3, -3, 1, -2, 5}};  /* elements 256..261 */
+  /* scores row 0: 3 4 6 7 1 6 -> heads 2, 3, 5 (ties: lower id first);
+   *        row 1: 4 2 3 3 7 7 -> heads 0, 4, 5 */
+  const int32_t want[B * K] = {2, 3, 5, 0, 4, 5};
+  uint16_t hx[B * D], hw[H * D];
+  memset(hx, 0, sizeof(hx));
+  memset(hw, 0, sizeof(hw));
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      hx[b * D + h] = f16_bits(xa[b][h]);
+      hx[b * D + 256 + h] = f16_bits(xb[b][h]);
+    }
+  for (int h = 0; h < H; ++h) hw[h * D + h] = hw[h * D + 256 + h] = f16_bits(1);
+  const size_t ws_bytes = sha_router_split_bytes(B, D, H, SHA_F16);
+  void *dx = NULL, *dw = NULL, *dws = NULL;
+  float* dsc = NULL;
+  int32_t* didx = NULL;
+  int ok = ws_bytes == (size_t)256 &&   /* 2 rows x 2 chunks x 6 heads x 4 B, rounded */
+           hip_ok(hipMalloc(&dx, sizeof(hx)), "hipMalloc x") &&
+           hip_ok(hipMalloc(&dw, sizeof(hw)), "hipMalloc w") &&
+           hip_ok(hipMalloc(&dws, ws_bytes), "hipMalloc workspace") &&
+           hip_ok(hipMalloc((void**)&dsc, B * H * sizeof(float)), "hipMalloc scores") &&
+           hip_ok(hipMalloc((void**)&didx, B * K * sizeof(int32_t)), "hipMalloc index") &&
+           hip_ok(hipMemcpy(dx, hx, sizeof(hx), hipMemcpyHostToDevice), "copy x") &&
+           hip_ok(hipMemcpy(dw, hw, sizeof(hw), hipMemcpyHostToDevice), "copy w");
+  if (ok) {
+    /* a workspace one byte short is refused before any launch */
+    ok = sha_router_topk_ex(dx, dw, NULL, B, D, H, K, didx, dsc, NULL, SHA_F16, dws,
+                            ws_bytes - 1) == SHA_ERR_WORKSPACE;
+    const sha_status st =
+        sha_router_topk_ex(dx, dw, NULL, B, D, H, K, didx, dsc, NULL, SHA_F16, dws, ws_bytes);
+    if (st != SHA_OK) {
+      fprintf(stderr, "sha_router_topk_ex: %s\n", sha_status_string(st));
+      ok = 0;
+    }
+  }
+  int32_t got[B * K];
+  float sc[B * H];
+  ok = ok && hip_ok(hipDeviceSynchronize(), "synchronize") &&
+       hip_ok(hipMemcpy(got, didx, sizeof(got), hipMemcpyDeviceToHost), "copy index back") &&
+       hip_ok(hipMemcpy(sc, dsc, sizeof(sc), hipMemcpyDeviceToHost), "copy scores back");
+  if (ok) {
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < H; ++h)
+        if (sc[b * H + h] != (float)(xa[b][h] + xb[b][h])) ok = 0;
+    for (int i = 0; i < B * K; ++i)
+      if (got[i] != want[i]) ok = 0;
+    printf("router (K-split, caller workspace): index [%d %d %d | %d %d %d], split scores "
+           "exact: %s\n",
+           got[0], got[1], got[2], got[3], got[4], got[5], ok ? "yes" : "no");
+  }
+  hipFree(dx);
+  hipFree(dw);
+  hipFree(dws);
+  hipFree(dsc);
+  hipFree(didx);
+  return ok;
+}
+
 int main(void) {
   /* Head-indexed: 2 rows, 6 heads, 2 selected per row; 3000 keys make the
    * library split the keys (and use its own workspace and combine). */
@@ -307,7 +387,8 @@ int main(void) {
   /* Group-indexed: 8 query heads in 2 groups of 4, one group per row. */
   const int32_t groups[2] = {1, 0};
   const int ok = run_case(0, 2, 6, 6, 3000, 64, 2, heads) &&
-                 run_case(1, 2, 8, 2, 777, 128, 1, groups) && run_router() && run_mlp();
+                 run_case(1, 2, 8, 2, 777, 128, 1, groups) && run_router() &&
+                 run_router_split() && run_mlp();
   printf("%s\n", ok ? "PASS" : "FAIL");
   return ok ? 0 : 1;
 }

@@ -3,7 +3,8 @@ decode_c.c) runs on the GPU: hipMalloc'd buffers, a head-indexed call whose
 keys the library splits (its own workspace, then the combine) and a
 group-indexed call, each checked against the closed form for q = 0 (outputs
 equal the mean of V) with unselected slots untouched; then the router on
-unit-vector weights (known scores and top-k) feeding a decode call, and the
+unit-vector weights (known scores and top-k) feeding a decode call, the
+router's K-split form with a caller workspace on f16 small integers, and the
 union + selective MLP on small integers, checked for exact equality."""
 import os
 import subprocess
@@ -26,4 +27,5 @@ def test_c_example_runs_and_passes():
     assert r.stdout.strip().splitlines()[-1] == "PASS"
     assert r.stdout.count("unselected slots untouched: yes") == 3
     assert "scores exact: yes" in r.stdout
+    assert "split scores exact: yes" in r.stdout
     assert "y exact" in r.stdout and "union: 5 neurons [3 7 12 30 39]" in r.stdout
