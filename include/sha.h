@@ -373,7 +373,9 @@ sha_status sha_selective_mlp(const void* x, const void* w1t, const void* w2t, co
  * page, ri.k117.org, "Software Dependencies").  A sha_step strings the sparse parts of one
  * decode step together for n_layers layers, in order, on one stream:
  *
- *   sparse layer: sha_router_topk(router_x, router_w, router_bias) -> index
+ *   sparse layer: sha_router_topk_ex(router_x, router_w, router_bias) -> index
+ *                 (the K-split form where sha_router_workspace_bytes picks it,
+ *                 in the step's own workspace)
  *                 sha_decode_kv / sha_decode_gqa_kv(q, k, v, index) -> o
  *   dense layer : sha_decode_kv / sha_decode_gqa_kv over every head (group)
  *   both, when mlp_w1t != NULL:
