@@ -243,6 +243,14 @@ def test_router_workspace_accounting_and_validation():
     def r(ws=P, ws_bytes=1 << 20, B=4, d=256, H=72, k=22, dtype=1, x=P):
         return L.sha_router_topk_ex(x, P, None, B, d, H, k, P, P, None, dtype, ws, ws_bytes)
 
+    # the binding's helper: the library's pick, any eligible shape, or none
+    f16 = bd.torch.float16
+    assert bd.router_workspace_bytes(64, 9216, 72, f16) == wsb(64, 9216, 72, 1) > 0
+    assert bd.router_workspace_bytes(16, 4096, 32, f16) == 0
+    assert bd.router_workspace_bytes(16, 4096, 32, f16, split=True) == sb(16, 4096, 32, 1) > 0
+    assert bd.router_workspace_bytes(64, 9216, 72, f16, split=False) == 0
+    assert bd.router_workspace_bytes(64, 9216, 72, bd.torch.float32, split=True) == 0
+
     need = sb(4, 256, 72, 1)
     assert r(ws_bytes=need - 1) == 4 and r(ws=P + 8) == 3
     assert r(k=73) == 1 and r(x=P + 8) == 3 and r(B=0, x=None, ws=None) == 0
